@@ -1,0 +1,239 @@
+"""Pins for the CPU oracle (CPU only).
+
+Each test checks the oracle against something other than itself: a
+hand-worked example, an independent pure-Python brute force, exhaustive
+enumeration, closed forms, invariants, or a library routine (numpy fp64
+matmul; torch's bf16 conversion).
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from workloads import make_random_small
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32(a):
+    return np.asarray(a, np.float32)
+
+
+# ------------------------------------------------------------ hand-worked example
+def test_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    e = g["expect"]
+    x, wg, wu, wd = (_f32(g[k]) for k in ("x", "wg_t", "wu_t", "wd"))
+    w, cap = g["tile_w"], g["cap"]
+    z = oracle.matmul_rows(x, np.arange(2), wg)
+    np.testing.assert_array_equal(z, np.asarray(e["z"], np.float64))
+    tw = oracle.pack_twell(z, w, cap, "f32")
+    np.testing.assert_array_equal(tw.cnt, np.asarray(e["cnt"]))
+    for t in range(2):
+        for b in range(2):
+            m = min(tw.cnt[t, b], cap)
+            assert list(tw.idx[t, b, :m]) == e["idx_kept"][t][b]
+            assert list(tw.val[t, b, :m]) == e["val_kept"][t][b]
+    row_ovf, rows, n = oracle.partition_overflow(tw.cnt, cap)
+    assert list(row_ovf) == e["row_ovf"] and list(rows) == e["ovf_rows"] and n == 1
+    np.testing.assert_array_equal(oracle.dense_backup(z, rows, "f32"), np.asarray(e["dense_backup"], np.float64))
+    np.testing.assert_array_equal(oracle.ffn_active(z, x, wu, wd), np.asarray(e["y_hybrid"], np.float64))
+    np.testing.assert_array_equal(oracle.ffn_twell(tw, x, wu, wd, skip_overflow=True),
+                                  np.asarray(e["y_fused_only"], np.float64))
+    # the brute force agrees with the same hand values
+    yb = brute.ffn(x.tolist(), wg.tolist(), wu.tolist(), wd.tolist())
+    np.testing.assert_array_equal(np.asarray(yb), np.asarray(e["y_hybrid"], np.float64))
+
+
+# ------------------------------------------------------------ exhaustive single tile
+def test_exhaustive_8wide_tile_all_caps():
+    """All 2^8 activity patterns of one 8-wide tile x capacities 1..8."""
+    pats = np.arange(256)
+    bits = ((pats[:, None] >> np.arange(8)[None, :]) & 1).astype(bool)
+    # active -> a distinct positive value, inactive -> negative, zero or NaN (all inactive)
+    inactive_fill = np.array([-1.0, 0.0, -0.0, np.nan, -np.inf])
+    z = np.where(bits, 1.0 + np.arange(8)[None, :] * 0.25,
+                 inactive_fill[np.arange(256)[:, None] % 5 + 0 * np.arange(8)[None, :]])
+    for cap in range(1, 9):
+        tw = oracle.pack_twell(z, 8, cap, "exact")
+        row_ovf, rows, n = oracle.partition_overflow(tw.cnt, cap)
+        for p in range(256):
+            set_cols = [c for c in range(8) if (p >> c) & 1]
+            assert tw.cnt[p, 0] == len(set_cols)
+            m = min(len(set_cols), cap)
+            assert list(tw.idx[p, 0, :m]) == set_cols[:cap]
+            assert list(tw.val[p, 0, :m]) == [1.0 + 0.25 * c for c in set_cols[:cap]]
+            assert row_ovf[p] == (1 if len(set_cols) > cap else 0)
+        assert list(rows) == [p for p in range(256) if bin(p).count("1") > cap]
+
+
+# ------------------------------------------------------------ brute force on tiny inputs
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("w", [4, 8])
+def test_against_brute_force(seed, w):
+    rng = np.random.default_rng(1000 + seed)
+    T = int(rng.integers(1, 5))
+    d = int(rng.integers(2, 9))
+    F = w * int(rng.integers(1, 32 // w + 1))
+    x = _f32(rng.integers(-8, 9, (T, d)) / 4)
+    wg = _f32(rng.integers(-8, 9, (F, d)) / 8)
+    wu = _f32(rng.integers(-8, 9, (F, d)) / 8)
+    wd = _f32(rng.integers(-8, 9, (F, d)) / 8)
+    zb = brute.matmul_nt(x.tolist(), wg.tolist())
+    z = oracle.matmul_rows(x, np.arange(T), wg)
+    np.testing.assert_array_equal(z, np.asarray(zb))
+    for cap in range(1, w + 1):
+        for vd in ("f32", "bf16"):
+            tw = oracle.pack_twell(z, w, cap, vd)
+            pb = brute.pack(zb, w, cap, vd)
+            for t in range(T):
+                for b in range(F // w):
+                    n, vals, cols = pb[t][b]
+                    assert tw.cnt[t, b] == n
+                    m = min(n, cap)
+                    assert list(tw.idx[t, b, :m]) == cols
+                    assert list(tw.val[t, b, :m]) == vals
+                    # unused slots are zero
+                    assert not tw.idx[t, b, m:].any() and not tw.val[t, b, m:].any()
+            _, rows, _ = oracle.partition_overflow(tw.cnt, cap)
+            assert list(rows) == brute.overflow_rows(pb, cap)
+    for hr in (None, "bf16"):
+        yb = np.asarray(brute.ffn(x.tolist(), wg.tolist(), wu.tolist(), wd.tolist(), hr))
+        y = oracle.ffn_active(z, x, wu, wd, hr)
+        np.testing.assert_allclose(y, yb, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------ rounding vs library routines
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal(200000).astype(np.float32) * np.float32(3.0) ** rng.integers(-30, 30, 200000)
+    # exact ties: upper 16 bits arbitrary, lower half exactly 0x8000
+    ties = (rng.integers(0, 2 ** 15, 5000).astype(np.uint32) << 16 | 0x8000).view(np.float32)
+    special = np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, 3.3895314e38, 1e-40, -1e-40], np.float32)
+    a = np.concatenate([a, ties[np.isfinite(ties)], special]).astype(np.float32)
+    want = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    got = oracle.store_round(a.astype(np.float64), "bf16").astype(np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    # NaN stays NaN (payloads are not compared: torch canonicalises them)
+    assert np.isnan(oracle.store_round(np.array([np.nan]), "bf16")).all()
+
+
+def test_f32_rounding_matches_numpy():
+    rng = np.random.default_rng(8)
+    a = rng.standard_normal(100000) * 10.0 ** rng.integers(-20, 20, 100000)
+    np.testing.assert_array_equal(oracle.store_round(a, "f32"), a.astype(np.float32).astype(np.float64))
+
+
+# ------------------------------------------------------------ dense == sparse, invariants
+@pytest.mark.parametrize("seed,w,cap,frac", [(0, 32, 4, 0.05), (1, 64, 8, 0.1), (2, 128, 16, 0.02),
+                                             (3, 32, 2, 0.2)])
+def test_dense_equals_sparse_bitwise_and_invariants(seed, w, cap, frac):
+    wl = make_random_small(T=37, d=64, F=4 * w, tile_w=w, cap=cap, active_frac=frac, seed=seed, jitter=0.5)
+    rows = np.arange(wl.T)
+    z = oracle.matmul_rows(wl.x, rows, wl.wg_t)
+    u = oracle.matmul_rows(wl.x, rows, wl.wu_t)
+    for hr in (None, "bf16"):
+        yd = oracle.ffn_dense(z, u, wl.wd, hr)
+        ys = oracle.ffn_active(z, wl.x, wl.wu_t, wl.wd, hr)
+        assert np.array_equal(yd, ys), "dense and sparse sums must agree bit for bit"
+    tw = oracle.pack_twell(z, w, cap, "bf16")
+    row_ovf, ovf_rows, n_ovf = oracle.partition_overflow(tw.cnt, cap)
+    nnz = int((z > 0).sum())
+    assert int(tw.cnt.sum()) == nnz                               # nonzero conservation
+    dense = oracle.dense_backup(z, ovf_rows, "bf16")
+    assert int(tw.cnt[row_ovf == 0].sum()) + int((dense > 0).sum()) == nnz  # hybrid conservation
+    ok = row_ovf == 0
+    h_stored = oracle.store_round(np.where(z > 0, z, 0.0), "bf16")
+    np.testing.assert_array_equal(oracle.unpack_twell(tw)[ok], h_stored[ok])  # round trip
+    # overflow tiles keep the cap lowest active columns
+    for t, b in zip(*np.nonzero(tw.cnt > cap)):
+        cols = np.nonzero(z[t, b * w:(b + 1) * w] > 0)[0][:cap]
+        np.testing.assert_array_equal(tw.idx[t, b], cols)
+    # fused-only output: non-overflow rows equal the full sum, overflow rows are 0
+    yf = oracle.ffn_twell(tw, wl.x, wl.wu_t, wl.wd, skip_overflow=True)
+    ys = oracle.ffn_active(z, wl.x, wl.wu_t, wl.wd, "bf16")
+    assert np.array_equal(yf[ok], ys[ok])
+    assert not yf[~ok].any()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_numpy_library_crosscheck(seed):
+    wl = make_random_small(T=50, d=128, F=512, tile_w=128, cap=8, active_frac=0.05, seed=seed)
+    z = oracle.matmul_rows(wl.x, np.arange(wl.T), wl.wg_t)
+    np.testing.assert_array_equal(z, oracle.gate(wl.x, wl.wg_t))  # exact on the grid
+    y = oracle.ffn_active(z, wl.x, wl.wu_t, wl.wd)
+    yn = oracle.ffn_numpy(wl.x, wl.wg_t, wl.wu_t, wl.wd)
+    np.testing.assert_allclose(y, yn, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ closed forms
+def test_closed_form_all_dead():
+    wl = make_random_small(T=20, d=64, F=256, tile_w=64, cap=4, active_frac=0.5, seed=3)
+    wl.wg_t[:, -1] = -np.inf
+    ref = oracle.reference(wl)
+    assert not ref.tw.cnt.any() and not ref.y_exact.any() and not ref.y_fused.any()
+    assert not np.isnan(ref.z).any()
+
+
+def test_closed_form_single_active_neuron():
+    wl = make_random_small(T=40, d=64, F=256, tile_w=64, cap=4, active_frac=0.5, seed=4)
+    j = 77
+    wl.wg_t[:, -1] = -np.inf
+    wl.wg_t[j, -1] = 1.0
+    ref = oracle.reference(wl)
+    zj = ref.z[:, j]
+    act = zj > 0
+    assert act.any() and (~act).any()
+    uj = wl.x.astype(np.float64) @ wl.wu_t[j].astype(np.float64)
+    want = np.where(act, zj, 0.0)[:, None] * uj[:, None] * wl.wd[j].astype(np.float64)[None, :]
+    np.testing.assert_allclose(ref.y_exact, want, rtol=1e-14, atol=0)
+    assert (ref.tw.cnt.sum(1) == act).all()
+    assert (ref.tw.idx[act, j // 64, 0] == j % 64).all()
+
+
+def test_closed_form_cap_equals_tile_all_active():
+    wl = make_random_small(T=16, d=64, F=128, tile_w=32, cap=32, active_frac=0.5, seed=5)
+    wl.wg_t[:, -1] = 64.0  # every pre-activation strictly positive
+    ref = oracle.reference(wl)
+    assert (ref.tw.cnt == 32).all()
+    assert (ref.tw.idx == np.arange(32)[None, None, :]).all()
+    np.testing.assert_array_equal(ref.tw.val.reshape(16, 128), oracle.store_round(ref.z, "bf16"))
+    np.testing.assert_allclose(ref.y_exact, oracle.ffn_numpy(wl.x, wl.wg_t, wl.wu_t, wl.wd), rtol=1e-12)
+
+
+def test_closed_form_identity_up_down():
+    """F = d, W_u = W_d = I  ->  y = ReLU(x W_g) * x."""
+    wl = make_random_small(T=24, d=64, F=64, tile_w=32, cap=32, active_frac=0.3, seed=6)
+    eye = np.eye(64, dtype=np.float32)
+    ref = oracle.reference(type(wl)(wl.name, wl.T, 64, 64, "bf16", 32, 32, wl.x, wl.wg_t, eye, eye))
+    want = np.where(ref.z > 0, ref.z, 0.0) * wl.x.astype(np.float64)
+    np.testing.assert_array_equal(ref.y_exact, want)
+
+
+def test_reference_rows_subset_consistent():
+    """Sampled-row reference equals the full reference restricted to those rows."""
+    wl = make_random_small(T=64, d=64, F=256, tile_w=64, cap=4, active_frac=0.08, seed=9, jitter=0.5)
+    full = oracle.reference(wl)
+    rows = np.array([3, 17, 18, 40, 63])
+    sub = oracle.reference(wl, rows)
+    np.testing.assert_array_equal(sub.tw.cnt, full.tw.cnt[rows])
+    np.testing.assert_array_equal(sub.y_exact, full.y_exact[rows])
+
+
+@pytest.mark.parametrize("w,cap", list(itertools.product([32, 256], [1, 16])))
+def test_nan_and_signed_zero_inactive(w, cap):
+    z = np.full((3, w), -1.0)
+    z[0, 0] = 0.0
+    z[0, 1] = -0.0
+    z[0, 2] = np.nan
+    z[1, 5] = 1e-30
+    z[2, w - 1] = 2.0
+    tw = oracle.pack_twell(z, w, cap, "f32")
+    assert tw.cnt[:, 0].tolist() == [0, 1, 1]
+    assert tw.idx[1, 0, 0] == 5 and tw.idx[2, 0, 0] == w - 1
