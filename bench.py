@@ -1,0 +1,240 @@
+"""Benchmark: sparse-FFN tokens/s of the TwELL path on one MI355X.
+
+One step = the whole hot path over one batch, all on one HIP stream:
+  twell_pack_gate          gate GEMM (bf16 MFMA) + ReLU + TwELL epilogue
+  twell_partition_overflow overflow flags, ascending overflow list, dense backup
+  twell_ffn_fused          fused up/down gather over the TwELL entries
+  twell_ffn_overflow       dense FFN of the overflow rows (hybrid part)
+Inputs (seeded, synthetic, grid mode) are resident in HBM before timing.
+
+Prints ONE JSON line (rank 0).  Default workload: the 2B-like layer
+(T=8192, d_model=2048, d_ff=8192, bf16, tile 256, capacity 16).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "sparse-FFN tokens/sec at 2B shape; HBM GB/s and MFMA util as % of peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer_2b")
+    ap.add_argument("--max-ovf", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    return ap.parse_args()
+
+
+def algorithmic(wl, ref_counts=None):
+    """Per-launch algorithmic work of each kernel (see the design notes)."""
+    T, d, F = wl.T, wl.d, wl.F
+    return {"gate_flop": 2.0 * T * d * F}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+                                   "not implemented", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import unstructured_sparse_transformer_amd as tw
+    from workloads import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tw.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    wl = make_workload(args.workload)
+    log(f"workload {wl.name}: T={wl.T} d={wl.d} F={wl.F} {wl.dtype} w={wl.tile_w} cap={wl.cap} "
+        f"(generated in {time.time() - t0:.1f}s)")
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)  # noqa: E731
+    x, wg, wu, wd = to(wl.x), to(wl.wg_t), to(wl.wu_t), to(wl.wd)
+    max_ovf = min(args.max_ovf, wl.T)
+    hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
+    ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt)
+    y = torch.empty((wl.T, wl.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        tw.twell_pack_gate(x, wg, hy.ell)
+        if ev:
+            ev[1].record()
+        tw.twell_partition_overflow(x, wg, hy)
+        if ev:
+            ev[2].record()
+        tw.twell_ffn_fused(hy.ell, x, wu, wd, y)
+        if ev:
+            ev[3].record()
+        tw.twell_ffn_overflow(hy, x, wu, wd, y, ws)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_ovf = int(hy.n_ovf.item())
+    if n_ovf > max_ovf:
+        raise SystemExit(f"n_ovf={n_ovf} exceeds max_ovf={max_ovf}; rerun with --max-ovf {n_ovf}")
+    cnt = hy.ell.cnt
+    kept = torch.clamp(cnt, max=wl.cap).sum(1)
+    ovf_mask = hy.row_ovf.bool()
+    entries = int(kept[~ovf_mask].sum().item())
+    nnz = int(cnt.sum().item())
+
+    # ---- timed region: K whole steps back to back, per-stage events inside
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(4)] for k in range(args.steps)])
+    stage_ms = stage.mean(0)
+    ms_per_step = wall * 1e3 / args.steps
+    value = wl.T * args.steps / wall
+
+    gate_flop = 2.0 * wl.T * wl.d * wl.F
+    gate_ms = float(stage_ms[0])
+    roofline = {"bound": "mfma", "kernel": "gate_twell_kernel (gate GEMM + TwELL epilogue)",
+                "achieved": round(gate_flop / (gate_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gate_flop / (gate_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+
+    # fused step: algorithmic bytes (per-token gather model and compulsory bytes)
+    esz = 2 if wl.dtype == "bf16" else 4
+    rows_twell = int((~ovf_mask).sum().item())
+    n_b = wl.F // wl.tile_w
+    gather_bytes = entries * 2 * wl.d * esz
+    per_token = rows_twell * (wl.d * esz + n_b * 4 + 4 * wl.d) + entries * (esz + 1)
+    kept_rows = hy.ell.idx  # noqa: F841  (union of active neurons computed on host below)
+    with torch.no_grad():
+        act = torch.zeros(wl.F, dtype=torch.bool, device=dev)
+        b = torch.arange(n_b, device=dev).view(1, n_b, 1) * wl.tile_w
+        slot = torch.arange(wl.cap, device=dev).view(1, 1, wl.cap)
+        valid = (slot < torch.clamp(cnt, max=wl.cap).unsqueeze(-1)) & (~ovf_mask).view(-1, 1, 1)
+        cols = (b + hy.ell.idx.long())[valid]
+        act[cols] = True
+        union = int(act.sum().item())
+    compulsory = union * 2 * wl.d * esz + per_token
+    fused_ms = float(stage_ms[2])
+    fused = {"kernel": "ffn_fused_kernel", "ms": round(fused_ms, 4), "entries": entries,
+             "gather_bytes": gather_bytes, "compulsory_bytes": compulsory,
+             "gather_GBps": round((gather_bytes + per_token) / (fused_ms * 1e-3) / 1e9, 1),
+             "compulsory_GBps": round(compulsory / (fused_ms * 1e-3) / 1e9, 1),
+             "compulsory_frac_hbm": round(compulsory / (fused_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded grid-mode inputs of the workload's shape and sparsity; no trained weights)",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
+                   "cap": wl.cap, "max_ovf": max_ovf, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "stages_ms": {"pack_gate": round(float(stage_ms[0]), 4), "partition_overflow": round(float(stage_ms[1]), 4),
+                      "ffn_fused": round(float(stage_ms[2]), 4), "ffn_overflow": round(float(stage_ms[3]), 4)},
+        "fused": fused,
+        "workload_stats": {"nnz": nnz, "n_ovf": n_ovf, "twell_entries": entries, "union_active_twell": union,
+                           "mean_active_per_token": round(nnz / wl.T, 2)},
+        "memory": {"twell_bytes": int(wl.T * n_b * (4 + wl.cap * (esz + 1))),
+                   "dense_backup_bytes": int(n_ovf * wl.F * esz), "dense_h_bytes": int(wl.T * wl.F * esz)},
+    }
+
+    # ---- cold-cache variant: flush MALL/L2 with a 1 GiB write between steps (outside the events)
+    if not args.no_cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold = []
+        for k in range(min(args.steps, 10)):
+            flush.fill_(float(k))
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            step(ev)
+            torch.cuda.synchronize()
+            cold.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
+        cold = np.array(cold).mean(0)
+        out["cold_cache_stages_ms"] = {"pack_gate": round(float(cold[0]), 4),
+                                       "partition_overflow": round(float(cold[1]), 4),
+                                       "ffn_fused": round(float(cold[2]), 4),
+                                       "ffn_overflow": round(float(cold[3]), 4),
+                                       "tokens_per_s": round(wl.T / (cold.sum() * 1e-3), 1)}
+        del flush
+
+    # ---- dense bf16 FFN on the same GPU (torch / hipBLASLt), comparator only
+    if not args.no_dense:
+        def dense_step():
+            z = torch.matmul(x, wg.t())
+            h = torch.relu(z) * torch.matmul(x, wu.t())
+            return torch.matmul(h, wd)
+        for _ in range(3):
+            dense_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            dense_step()
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.steps
+        out["dense_bf16_ffn"] = {"ms_per_step": round(dms, 4), "tokens_per_s": round(wl.T / (dms * 1e-3), 1),
+                                 "tflops": round(3 * gate_flop / (dms * 1e-3) / 1e12, 1),
+                                 "sparse_speedup": round(dms / ms_per_step, 3)}
+
+    # ---- CPU oracle on a bounded sample of the same workload (rank 0, N=1)
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+        def oracle_step(rows):
+            sub = wl.rows(0, rows)
+            z = oracle.gate(sub.x, sub.wg_t)
+            t = oracle.pack_twell(z, sub.tile_w, sub.cap, sub.dtype)
+            _, ovf_rows, _ = oracle.partition_overflow(t.cnt, sub.cap)
+            oracle.dense_backup(z, ovf_rows, sub.dtype)
+            oracle.ffn_active(z, sub.x, sub.wu_t, sub.wd, sub.dtype)
+
+        n = min(256, wl.T)
+        t1 = time.perf_counter()
+        oracle_step(n)
+        dt1 = time.perf_counter() - t1
+        n2 = int(min(wl.T, max(n, n * args.cpu_seconds / max(dt1, 1e-3))))
+        n2 = max(n, (n2 // 256) * 256)
+        t2 = time.perf_counter()
+        oracle_step(n2)
+        dt2 = time.perf_counter() - t2
+        out["cpu_baseline"] = {"value": round(n2 / dt2, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                               "sample": f"first {n2} of {wl.T} tokens of {wl.name}: fp64 numpy gate + C TwELL "
+                                         f"packer, partition, dense backup and fused sum ({dt2:.1f} s)"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

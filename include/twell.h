@@ -1,0 +1,160 @@
+/*
+ * twell.h -- C ABI of libtwell: the ReLU-sparse gated FFN inference path on
+ * MI355X (gfx950), with its activations held in TwELL (tile-wise ELLPACK).
+ *
+ * Source of the method: "Sparser, Faster, Lighter Transformer Language Models"
+ * (gist.science summary page).  Section 2.1 defines TwELL and its production
+ * in the gate matmul's epilogue; section 2.2 the fused up/down inference
+ * kernel; section 2.3 the hybrid ELL + dense-backup format for rows whose
+ * nonzeros do not fit.  The page gives no API; the calls below are this
+ * library's own.
+ *
+ * Notation: T tokens (rows), d model width, F hidden width (d_ff), w tile
+ * width, n_b = F / w tiles per row, cap = slots per (row, tile).
+ *   z = x . W_g  (fp32 accumulation),  h_g = ReLU(z),  u = x . W_u,
+ *   y = (h_g * u) . W_d                                  (y in fp32)
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument inside the structs and every x / weight / y
+ *     pointer is DEVICE memory owned by the caller; the struct itself lives in
+ *     host memory and is read during the call only.  The library never
+ *     allocates, frees or synchronises: work is queued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and the call returns at once.
+ *   - Layouts are row-major.  Weights come as W_g^T, W_u^T and W_d, each
+ *     [F][d]: the three weight vectors of hidden neuron j are contiguous rows
+ *     of d elements.  x is [T][d], y is [T][d] float.
+ *   - Element type (vdtype) of x, the weights, TwELL values and the dense
+ *     backup: TWELL_BF16 (bf16 inputs, fp32 accumulation) or TWELL_F32.
+ *   - A gate value is active iff its fp32 accumulator is > 0 (0, -0 and NaN
+ *     are inactive).  Inside a tile, entries appear in ascending column order.
+ *     cnt holds the TRUE number of actives of a (row, tile), which may exceed
+ *     cap; only the cap lowest columns are stored.  Slots at or past
+ *     min(cnt, cap) are left untouched (undefined content).
+ *   - Inputs must be finite, except that the bias column of W_g^T may hold
+ *     -inf (a dead neuron: never active).
+ *   - Errors the host can see return a negative status BEFORE anything is
+ *     queued: NULL pointer, pointer not 16-byte aligned, bad shape, unsupported
+ *     tile width / capacity / dtype, workspace too small.  A failed launch
+ *     returns TWELL_E_HIP.  Overflow is data, not an error.
+ *   - No C++ exception crosses this interface; the library keeps no mutable
+ *     global state.  Concurrent calls on different streams are safe when their
+ *     output buffers do not overlap.
+ */
+#ifndef TWELL_H
+#define TWELL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define TWELL_API __attribute__((visibility("default")))
+#else
+#define TWELL_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum twell_status {
+    TWELL_OK = 0,
+    TWELL_E_NULL = -1,        /* a required pointer is NULL */
+    TWELL_E_ALIGN = -2,       /* a device pointer is not 16-byte aligned */
+    TWELL_E_SHAPE = -3,       /* T < 0, T*n_b too large, d % 64 != 0, F % tile_w != 0, ... */
+    TWELL_E_UNSUPPORTED = -4, /* tile_w not in {32,64,128,256}, cap not in [1, tile_w], dtype */
+    TWELL_E_HIP = -5,         /* the HIP runtime refused a launch */
+    TWELL_E_WORKSPACE = -6    /* workspace pointer NULL or smaller than required */
+};
+
+enum twell_dtype { TWELL_F32 = 0, TWELL_BF16 = 1 };
+
+/* TwELL activations (section 2.1 of the page: per (row, tile) a count, packed
+ * values and tile-local indices). */
+typedef struct twell_t {
+    int32_t T;      /* rows (tokens), >= 0 */
+    int32_t F;      /* columns (hidden width), multiple of tile_w */
+    int32_t tile_w; /* tile width w: 32, 64, 128 or 256 */
+    int32_t cap;    /* slots per (row, tile): 1 <= cap <= tile_w */
+    int32_t vdtype; /* enum twell_dtype of val (and of x and the weights) */
+    int32_t reserved;
+    void *val;      /* device [T][n_b][cap] activation values h_g, vdtype */
+    uint8_t *idx;   /* device [T][n_b][cap] tile-local column 0..w-1 */
+    int32_t *cnt;   /* device [T][n_b] true active count per (row, tile) */
+} twell_t;
+
+/* Hybrid ELL + dense backup (section 2.3 of the page).  A row is an overflow
+ * row iff some tile of it has cnt > cap; such rows are listed in ascending
+ * token order and their full h_g rows are kept densely. */
+typedef struct twell_hybrid_t {
+    twell_t ell;       /* TwELL of all rows */
+    int32_t max_ovf;   /* rows available in ovf_rows / dense, >= 0 */
+    int32_t reserved;
+    int32_t *row_ovf;  /* device [T]: 1 for an overflow row, else 0 */
+    int32_t *ovf_rows; /* device [max_ovf]: overflow rows, ascending */
+    int32_t *n_ovf;    /* device [1]: number of overflow rows (may exceed max_ovf) */
+    void *dense;       /* device [max_ovf][F] vdtype: h_g rows of the overflow tokens */
+} twell_hybrid_t;
+
+/* Gate GEMM with the TwELL epilogue (section 2.1 of the page: x . W_g, ReLU
+ * and packing into TwELL done in the matmul's epilogue, with no separate
+ * conversion pass).
+ *   x    : device [h->T][d], vdtype h->vdtype
+ *   wg_t : device [h->F][d], vdtype h->vdtype (column d-1 may hold -inf)
+ *   d    : model width, multiple of 64
+ *   h    : output TwELL; writes h->cnt fully and the kept slots of h->val,
+ *          h->idx.
+ * Returns TWELL_OK or a negative twell_status. */
+TWELL_API int twell_pack_gate(const void *x, const void *wg_t, int32_t d, const twell_t *h, void *stream);
+
+/* Overflow partition and dense backup (section 2.3 of the page): from
+ * hy->ell.cnt (written by twell_pack_gate) computes row_ovf, the ascending
+ * ovf_rows list and n_ovf, then recomputes ReLU(x . W_g) for the first
+ * min(n_ovf, max_ovf) overflow rows into hy->dense.  Rows past max_ovf are
+ * counted in n_ovf but get no dense row: the caller checks n_ovf <= max_ovf
+ * after synchronising and retries with larger buffers otherwise. */
+TWELL_API int twell_partition_overflow(const void *x, const void *wg_t, int32_t d,
+                             const twell_hybrid_t *hy, void *stream);
+
+/* twell_pack_gate on hy->ell followed by twell_partition_overflow. */
+TWELL_API int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d,
+                           const twell_hybrid_t *hy, void *stream);
+
+/* Fused up/down projection from TwELL (section 2.2 of the page): for every
+ * row and every stored entry (b, s), j = b*w + idx:  u = x[t] . W_u^T[j]
+ * (fp32), y[t] += (val * u) * W_d[j] (fp32).  Only the kept rows of W_u^T
+ * and W_d are read.  Rows with some cnt > cap (overflow rows) get y = 0;
+ * rows without actives get y = 0.
+ *   x, wu_t, wd : device, vdtype h->vdtype;  y : device [h->T][d] float. */
+TWELL_API int twell_ffn_fused(const twell_t *h, const void *x, const void *wu_t, const void *wd,
+                    int32_t d, float *y, void *stream);
+
+/* Bytes of device workspace twell_ffn_hybrid needs for these sizes. */
+TWELL_API size_t twell_ffn_hybrid_workspace_bytes(int32_t max_ovf, int32_t F, int32_t d, int32_t vdtype);
+
+/* Dense part of the hybrid FFN (section 2.3 of the page): for the first
+ * min(n_ovf, max_ovf) overflow rows r = ovf_rows[i], writes
+ * y[r] = (dense[i] * (x[r] . W_u)) . W_d, the gated product rounded to
+ * vdtype before the down projection (fp32 accumulation).  Other y rows are
+ * not touched.  Expects hy filled by twell_pack_gate_hybrid on the same
+ * stream.  workspace: device, >= twell_ffn_hybrid_workspace_bytes(...),
+ * 256-byte aligned, content ignored on entry. */
+TWELL_API int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
+                       int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Hybrid FFN: twell_ffn_fused for all rows (overflow rows get 0), then
+ * twell_ffn_overflow for the overflow rows; every row of y is the full FFN
+ * output when n_ovf <= max_ovf. */
+TWELL_API int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
+                     int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+TWELL_API const char *twell_status_str(int status);
+
+/* Library ABI version (major * 100 + minor). */
+TWELL_API int twell_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWELL_H */

@@ -1,0 +1,121 @@
+"""Shared test helpers: run the HIP path through the binding and compare it
+with the oracle.  Imported by the test modules only."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+# y tolerance: per row, ||y_gpu - y_ref||_2 <= 1e-2 ||y_ref||_2 against the oracle's
+# exact-h sum (bf16 inputs, fp32 accumulation); rows without actives exactly 0.
+Y_RTOL = 1e-2
+# Tighter check against the oracle's stored-h sum for TwELL rows: the only
+# differences left are fp32 rounding and summation order in the fused step.
+Y_RTOL_STORED = 1e-4
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(wl):
+    import torch
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = "cuda"
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev).to(dt)  # noqa: E731
+    return dt, f(wl.x), f(wl.wg_t), f(wl.wu_t), f(wl.wd)
+
+
+def run_hip(wl, max_ovf=None, stream=None):
+    """Run pack_gate_hybrid + ffn_hybrid and (separately) ffn_fused; return host arrays."""
+    import torch
+    import unstructured_sparse_transformer_amd as tw
+    dt, x, wg, wu, wd = to_device(wl)
+    if max_ovf is None:
+        max_ovf = wl.T
+    hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
+    # poison the outputs so stale memory cannot pass a check
+    hy.ell.cnt.fill_(-7)
+    hy.row_ovf.fill_(-7)
+    hy.n_ovf.fill_(-7)
+    y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    yf = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt)
+    tw.twell_pack_gate_hybrid(x, wg, hy, stream)
+    tw.twell_ffn_hybrid(hy, x, wu, wd, y, ws, stream)
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, yf, stream)
+    torch.cuda.synchronize()
+    n_ovf = int(hy.n_ovf.item())
+    m = min(n_ovf, max_ovf)
+    return {
+        "cnt": hy.ell.cnt.cpu().numpy(),
+        "val": hy.ell.val.float().cpu().numpy(),
+        "idx": hy.ell.idx.cpu().numpy(),
+        "row_ovf": hy.row_ovf.cpu().numpy(),
+        "n_ovf": n_ovf,
+        "ovf_rows": hy.ovf_rows[:m].cpu().numpy(),
+        "dense": hy.dense[:m].float().cpu().numpy(),
+        "y": y.cpu().numpy(),
+        "y_fused": yf.cpu().numpy(),
+        "max_ovf": max_ovf,
+    }
+
+
+def row_rel_err(a, b):
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    return num, den
+
+
+def compare(wl, out, ref=None, rows=None, check_y=True, label=""):
+    """Assert GPU == oracle: TwELL bit-exact (counts, kept indices and values),
+    partition and dense backup exact, y within the stated tolerance."""
+    if ref is None:
+        ref = oracle.reference(wl, rows)
+    rows = ref.rows
+    cnt = out["cnt"][rows]
+    np.testing.assert_array_equal(cnt, ref.tw.cnt, err_msg=f"{label}: TwELL counts")
+    kept = ref.tw.kept()
+    np.testing.assert_array_equal(out["idx"][rows][kept], ref.tw.idx[kept], err_msg=f"{label}: TwELL indices")
+    np.testing.assert_array_equal(out["val"][rows][kept], ref.tw.val[kept].astype(np.float32),
+                                  err_msg=f"{label}: TwELL values")
+    np.testing.assert_array_equal(out["row_ovf"][rows], ref.row_ovf, err_msg=f"{label}: row_ovf")
+    # the overflow list is a property of all rows: it must be exactly the ascending list
+    # of rows whose GPU counts exceed cap (checked against the oracle's flags on `rows`)
+    all_ovf = np.nonzero((out["cnt"] > wl.cap).any(1))[0]
+    assert out["n_ovf"] == len(all_ovf), f"{label}: n_ovf {out['n_ovf']} vs {len(all_ovf)}"
+    m = min(out["n_ovf"], out["max_ovf"])
+    np.testing.assert_array_equal(out["ovf_rows"], all_ovf[:m], err_msg=f"{label}: ovf_rows")
+    # dense backup rows for the overflow rows covered by `rows`
+    pos = {int(t): i for i, t in enumerate(out["ovf_rows"])}
+    for li in ref.ovf_local:
+        t = int(rows[li])
+        if t in pos:
+            want = oracle.dense_backup(ref.z[li:li + 1], [0], wl.dtype)[0]
+            np.testing.assert_array_equal(out["dense"][pos[t]], want.astype(np.float32),
+                                          err_msg=f"{label}: dense backup row {t}")
+    if not check_y:
+        return ref
+    y = out["y"][rows].astype(np.float64)
+    yf = out["y_fused"][rows].astype(np.float64)
+    assert np.isfinite(y).all() and np.isfinite(yf).all(), f"{label}: non-finite y"
+    covered = np.array([(int(t) in pos) or not ref.row_ovf[i] for i, t in enumerate(rows)])
+    num, den = row_rel_err(y, ref.y_exact)
+    zero = den == 0
+    assert not y[zero & covered].any(), f"{label}: rows without actives must be exactly 0"
+    bad = covered & ~zero & (num > Y_RTOL * den)
+    assert not bad.any(), f"{label}: y rows off by more than {Y_RTOL}: {np.nonzero(bad)[0][:10]} " \
+                          f"max rel {np.max(num[~zero] / den[~zero]):.3g}"
+    # fused-only: overflow rows are 0, TwELL rows equal the hybrid's TwELL rows bit for bit
+    ok = ref.row_ovf == 0
+    assert not yf[~ok].any(), f"{label}: fused-only output must zero overflow rows"
+    np.testing.assert_array_equal(yf[ok], y[ok], err_msg=f"{label}: fused vs hybrid TwELL rows")
+    num2, den2 = row_rel_err(yf[ok], ref.y_stored[ok])
+    nz = den2 > 0
+    tight = num2[nz] <= Y_RTOL_STORED * den2[nz]
+    assert tight.all(), f"{label}: fused y vs stored-h oracle: max rel {np.max(num2[nz] / den2[nz]):.3g}"
+    return ref

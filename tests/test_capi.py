@@ -1,0 +1,91 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+symbol include/twell.h declares, and rejects bad arguments before launching."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import unstructured_sparse_transformer_amd as tw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "twell.h")).read()
+    return sorted(set(re.findall(r"TWELL_API\s+[\w\s\*]+?\b(twell_\w+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    lib = tw.load()
+    names = _declared()
+    assert set(names) == set(tw.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.twell_version() == 100
+
+
+def test_status_strings():
+    lib = tw.load()
+    for st in range(0, -7, -1):
+        assert lib.twell_status_str(st)
+    assert lib.twell_status_str(-99) == b"unknown status"
+
+
+def _desc(T=16, F=512, w=128, cap=8, vd=1, val=256, idx=512, cnt=1024):
+    return tw.TwellT(T, F, w, cap, vd, 0, val, idx, cnt)
+
+
+GOOD = 4096  # an aligned, never dereferenced fake device address
+
+
+def test_pack_gate_validation():
+    lib = tw.load()
+    f = lib.twell_pack_gate
+    assert f(GOOD, GOOD, 64, None, None) == -1
+    assert f(None, GOOD, 64, ctypes.byref(_desc()), None) == -1             # x NULL
+    assert f(GOOD, None, 64, ctypes.byref(_desc()), None) == -1             # W_g NULL
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(val=0)), None) == -1        # val NULL
+    assert f(GOOD + 8, GOOD, 64, ctypes.byref(_desc()), None) == -2         # x misaligned
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(cnt=1026)), None) == -2     # cnt misaligned
+    assert f(GOOD, GOOD, 65, ctypes.byref(_desc()), None) == -3             # d % 64
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(F=500)), None) == -3        # F % w
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(F=96, w=32)), None) == -3   # F % 64
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(T=-1)), None) == -3
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(w=100)), None) == -4        # tile width
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(w=512, F=1024)), None) == -4
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(cap=0)), None) == -4
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(cap=129)), None) == -4
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(vd=2)), None) == -4
+    assert f(GOOD, GOOD, 8192, ctypes.byref(_desc()), None) == -4           # bf16 row > 8 KiB
+    assert f(GOOD, GOOD, 4096, ctypes.byref(_desc(vd=0)), None) == -4       # f32 row > 8 KiB
+    assert f(None, None, 64, ctypes.byref(_desc(T=0)), None) == 0           # T = 0: nothing to do
+
+
+def test_fused_and_hybrid_validation():
+    lib = tw.load()
+    d = _desc()
+    assert lib.twell_ffn_fused(ctypes.byref(d), GOOD, GOOD, GOOD, 64, None, None) == -1   # y NULL
+    assert lib.twell_ffn_fused(ctypes.byref(d), GOOD, GOOD, GOOD + 4, 64, GOOD, None) == -2
+    assert lib.twell_ffn_fused(ctypes.byref(d), GOOD, GOOD, GOOD, 60, GOOD, None) == -3
+    hy = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD)
+    need = lib.twell_ffn_hybrid_workspace_bytes(8, 512, 64, 1)
+    assert need > 0
+    assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, None, 0, None) == -6
+    assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, GOOD, need - 1, None) == -6
+    assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, GOOD + 16, need, None) == -2
+    bad = tw.TwellHybridT(d, -1, 0, GOOD, GOOD, GOOD, GOOD)
+    assert lib.twell_partition_overflow(GOOD, GOOD, 64, ctypes.byref(bad), None) == -3
+    nod = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, None)
+    assert lib.twell_pack_gate_hybrid(GOOD, GOOD, 64, ctypes.byref(nod), None) == -1
+    assert lib.twell_partition_overflow(GOOD, GOOD, 64, None, None) == -1
+    assert lib.twell_ffn_hybrid_workspace_bytes(0, 512, 64, 1) == 0
+
+
+def test_binding_requires_library(tmp_path, monkeypatch):
+    """No CPU fallback: a missing library is an error."""
+    tw.load()
+    monkeypatch.setattr(tw, "_lib", None)
+    with pytest.raises(RuntimeError, match="libtwell.so not found"):
+        tw.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+TwELL counts, kept indices and values, the overflow partition and the dense
+backup must match bit for bit (grid-mode inputs make z exact in fp32 on both
+sides); y must be within 1e-2 of the oracle's exact sum per row (and within
+1e-4 of its stored-h sum on TwELL rows).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import compare, run_hip, say
+from workloads import (make_decode_windows, make_layer_0p5b, make_layer_2b, make_random_small,
+                       make_stress_layer, make_tiny)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_fp32(gpu_lib):
+    wl = make_tiny()
+    say(f"case tiny T={wl.T} d={wl.d} F={wl.F} f32")
+    out = run_hip(wl)
+    compare(wl, out, label="tiny")
+    assert out["n_ovf"] == 0
+
+
+def test_layer_0p5b(gpu_lib):
+    wl = make_layer_0p5b()
+    say(f"case layer_0p5b T={wl.T} d={wl.d} F={wl.F} bf16")
+    out = run_hip(wl, max_ovf=256)
+    compare(wl, out, label="0p5b")
+
+
+def test_layer_2b_full(gpu_lib):
+    wl = make_layer_2b()
+    say(f"case layer_2b T={wl.T} d={wl.d} F={wl.F} bf16 (full oracle)")
+    out = run_hip(wl, max_ovf=1024)
+    ref = compare(wl, out, label="2b")
+    say(f"  n_ovf={out['n_ovf']} nnz={int(ref.tw.cnt.sum())} mean/row={ref.tw.cnt.sum(1).mean():.2f}")
+    assert 100 < out["n_ovf"] < 400
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_decode_windows(gpu_lib, T):
+    wins = make_decode_windows(T, max_windows=512)
+    # windows with the most actives first, plus a few from the start
+    base = make_layer_2b()
+    z_sample = oracle.gate(base.x[: len(wins) * T], base.wg_t)
+    act = (z_sample > 0).reshape(len(wins), T, -1).sum((1, 2))
+    pick = sorted(set([0, 1, 2] + list(np.argsort(-act)[:5])))
+    for i in pick:
+        wl = wins[i]
+        say(f"case decode T={T} window={i}")
+        out = run_hip(wl, max_ovf=T)
+        compare(wl, out, label=f"decode T={T} w={i}")
+
+
+@pytest.mark.parametrize("layer", [0, 23])
+def test_stress_layer_full(gpu_lib, layer):
+    wl = make_stress_layer(layer)
+    say(f"case stress layer {layer} T={wl.T} (full oracle)")
+    out = run_hip(wl, max_ovf=1024)
+    compare(wl, out, label=f"stress l{layer}")
+    n_stress = len(wl.meta["stress_rows"])
+    assert out["n_ovf"] >= 0.9 * n_stress
+
+
+@pytest.mark.parametrize("layer", [6, 12, 18])
+def test_stress_layer_sampled(gpu_lib, layer):
+    wl = make_stress_layer(layer)
+    rng = np.random.default_rng(layer)
+    rows = np.union1d(rng.choice(wl.T, 384, replace=False), wl.meta["stress_rows"][:64])
+    say(f"case stress layer {layer} sampled rows={len(rows)}")
+    out = run_hip(wl, max_ovf=1024)
+    compare(wl, out, rows=rows, label=f"stress l{layer} sampled")
+
+
+EDGE = [
+    # (T, d, F, w, cap, dtype, frac, jitter, dead)
+    (300, 128, 512, 128, 8, "bf16", 0.05, 0.5, 0),     # ragged T (not a multiple of 256)
+    (257, 64, 384, 128, 4, "bf16", 0.08, 0.5, 0),      # F not a multiple of 256, d = 64
+    (100, 256, 1024, 32, 4, "bf16", 0.1, 0.5, 0),      # w = 32
+    (100, 256, 1024, 64, 2, "bf16", 0.1, 0.5, 30),     # w = 64, dead neurons
+    (130, 512, 2048, 256, 1, "bf16", 0.05, 0.5, 0),    # cap = 1
+    (64, 4096, 512, 256, 16, "bf16", 0.05, 0.5, 0),    # d = 4096 (largest bf16 row)
+    (70, 2048, 512, 128, 8, "f32", 0.1, 0.5, 0),       # fp32, largest fp32 row
+    (90, 192, 640, 64, 8, "f32", 0.2, 0.3, 5),         # fp32 odd shapes
+    (512, 256, 1024, 128, 3, "bf16", 0.4, 0.2, 0),     # nearly every row overflows
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}_d{c[1]}_F{c[2]}_w{c[3]}_c{c[4]}_{c[5]}" for c in EDGE])
+def test_edge_shapes(gpu_lib, case):
+    T, d, F, w, cap, dt, frac, jit, dead = case
+    wl = make_random_small(T, d, F, w, cap, dt, active_frac=frac, seed=T + d, jitter=jit, n_dead=dead)
+    say(f"case edge {wl.name}")
+    out = run_hip(wl)
+    compare(wl, out, label=wl.name)
+
+
+def test_all_dead(gpu_lib):
+    wl = make_random_small(200, 256, 1024, 256, 16, "bf16", active_frac=0.3, seed=11)
+    wl.wg_t[:, -1] = -np.inf
+    say("case all-dead (bias -inf everywhere)")
+    out = run_hip(wl)
+    assert not out["cnt"].any() and out["n_ovf"] == 0
+    assert not out["y"].any() and not out["y_fused"].any()
+
+
+def test_dense_tile_all_active(gpu_lib):
+    """cap = w with every pre-activation positive: TwELL is the dense h_g."""
+    wl = make_random_small(96, 128, 256, 32, 32, "bf16", active_frac=0.5, seed=12)
+    wl.wg_t[:, -1] = 64.0
+    say("case dense tile, all active")
+    out = run_hip(wl)
+    ref = compare(wl, out, label="all-active")
+    assert (out["cnt"] == 32).all() and out["n_ovf"] == 0
+    assert (out["idx"] == np.arange(32)[None, None, :]).all()
+
+
+def test_single_active_neuron(gpu_lib):
+    wl = make_random_small(128, 256, 512, 128, 4, "bf16", active_frac=0.5, seed=13)
+    wl.wg_t[:, -1] = -np.inf
+    wl.wg_t[300, -1] = 1.0
+    say("case single active neuron")
+    out = run_hip(wl)
+    compare(wl, out, label="single neuron")
+    assert set(np.unique(out["cnt"].sum(1))) <= {0, 1}
+
+
+def test_overflow_beyond_max_ovf(gpu_lib):
+    """n_ovf > max_ovf: n_ovf is the true count, the first max_ovf rows are served."""
+    wl = make_random_small(256, 128, 512, 128, 2, "bf16", active_frac=0.3, seed=14)
+    ref = oracle.reference(wl)
+    n_true = len(ref.ovf_local)
+    assert n_true > 20
+    say(f"case max_ovf=16 < n_ovf={n_true}")
+    out = run_hip(wl, max_ovf=16)
+    assert out["n_ovf"] == n_true
+    np.testing.assert_array_equal(out["ovf_rows"], ref.ovf_local[:16])
+    compare(wl, out, ref=ref, check_y=False, label="truncated")
+    served = ref.ovf_local[:16]
+    num = np.linalg.norm(out["y"][served] - ref.y_exact[served], axis=1)
+    assert (num <= 1e-2 * np.linalg.norm(ref.y_exact[served], axis=1)).all()
+    unserved = ref.ovf_local[16:]
+    assert not out["y"][unserved].any()
+
+
+def test_zero_rows(gpu_lib):
+    import torch
+    import unstructured_sparse_transformer_amd as tw
+    say("case T = 0")
+    hy = tw.Hybrid.empty(0, 512, 128, 8, torch.bfloat16, 0)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((512, 128), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((0, 128), dtype=torch.float32, device="cuda")
+    tw.twell_pack_gate_hybrid(x, w, hy)
+    tw.twell_ffn_hybrid(hy, x, w, w, y, None)
+    torch.cuda.synchronize()
+
+
+def test_deterministic_and_stream(gpu_lib):
+    """Same bits on a second run, on a non-default stream."""
+    import torch
+    wl = make_random_small(600, 512, 2048, 256, 16, "bf16", active_frac=0.02, seed=15, jitter=0.5)
+    say("case determinism")
+    a = run_hip(wl)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_hip(wl, stream=s)
+    for k in ("cnt", "row_ovf", "y", "y_fused", "dense"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    kept = oracle.reference(wl).tw.kept()
+    np.testing.assert_array_equal(a["val"][kept], b["val"][kept])

@@ -1,0 +1,212 @@
+"""Python binding of libtwell (ReLU-sparse gated FFN with TwELL on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libtwell.so`` (built from ``csrc/`` by ``_build.py``); PyTorch supplies device
+memory and the current HIP stream.  There is no CPU fallback: ``load()``
+raises when the library is missing, and every call raises on a non-OK status.
+
+The functions carry the C names (``include/twell.h``):
+``twell_pack_gate``, ``twell_partition_overflow``, ``twell_pack_gate_hybrid``,
+``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
+``twell_ffn_hybrid_workspace_bytes``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtwell.so")
+
+TWELL_F32, TWELL_BF16 = 0, 1
+STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_SHAPE",
+          -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE"}
+EXPORTS = ("twell_pack_gate", "twell_partition_overflow", "twell_pack_gate_hybrid", "twell_ffn_fused",
+           "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid", "twell_status_str",
+           "twell_version")
+
+
+class TwellT(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("F", ctypes.c_int32), ("tile_w", ctypes.c_int32),
+                ("cap", ctypes.c_int32), ("vdtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("val", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("cnt", ctypes.c_void_p)]
+
+
+class TwellHybridT(ctypes.Structure):
+    _fields_ = [("ell", TwellT), ("max_ovf", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("row_ovf", ctypes.c_void_p), ("ovf_rows", ctypes.c_void_p), ("n_ovf", ctypes.c_void_p),
+                ("dense", ctypes.c_void_p)]
+
+
+class TwellError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.twell_status_str(status).decode() if _lib is not None else ""
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libtwell.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libtwell.so not found at {path}: build it with "
+                           "`python -m unstructured_sparse_transformer_amd._build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(path)
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    lib.twell_pack_gate.argtypes = [P, P, I32, ctypes.POINTER(TwellT), P]
+    lib.twell_partition_overflow.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
+    lib.twell_pack_gate_hybrid.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
+    lib.twell_ffn_fused.argtypes = [ctypes.POINTER(TwellT), P, P, P, I32, P, P]
+    lib.twell_ffn_hybrid_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.twell_ffn_hybrid_workspace_bytes.restype = ctypes.c_size_t
+    lib.twell_ffn_hybrid.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
+    lib.twell_ffn_overflow.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
+    lib.twell_status_str.argtypes = [ctypes.c_int]
+    lib.twell_status_str.restype = ctypes.c_char_p
+    lib.twell_version.restype = ctypes.c_int
+    for fn in (lib.twell_pack_gate, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
+               lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow):
+        fn.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- marshalling helpers
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def vdtype_of(torch_dtype) -> int:
+    import torch
+    if torch_dtype == torch.bfloat16:
+        return TWELL_BF16
+    if torch_dtype == torch.float32:
+        return TWELL_F32
+    raise TypeError(f"unsupported element type {torch_dtype}")
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise TwellError(fn, st)
+
+
+@dataclass
+class TwELL:
+    """Device buffers of one TwELL (torch tensors) and its C descriptor."""
+    T: int
+    F: int
+    tile_w: int
+    cap: int
+    dtype: object
+    val: object  # [T][n_b][cap] dtype
+    idx: object  # [T][n_b][cap] uint8
+    cnt: object  # [T][n_b] int32
+
+    @property
+    def n_b(self) -> int:
+        return self.F // self.tile_w
+
+    @classmethod
+    def empty(cls, T, F, tile_w, cap, dtype, device="cuda"):
+        import torch
+        n_b = F // tile_w
+        return cls(T, F, tile_w, cap, dtype,
+                   torch.empty((T, n_b, cap), dtype=dtype, device=device),
+                   torch.empty((T, n_b, cap), dtype=torch.uint8, device=device),
+                   torch.empty((T, n_b), dtype=torch.int32, device=device))
+
+    def desc(self) -> TwellT:
+        return TwellT(self.T, self.F, self.tile_w, self.cap, vdtype_of(self.dtype), 0,
+                      _ptr(self.val), _ptr(self.idx), _ptr(self.cnt))
+
+
+@dataclass
+class Hybrid:
+    """TwELL plus overflow partition and dense backup buffers."""
+    ell: TwELL
+    max_ovf: int
+    row_ovf: object   # [T] int32
+    ovf_rows: object  # [max_ovf] int32
+    n_ovf: object     # [1] int32
+    dense: object     # [max_ovf][F] dtype
+
+    @classmethod
+    def empty(cls, T, F, tile_w, cap, dtype, max_ovf, device="cuda"):
+        import torch
+        return cls(TwELL.empty(T, F, tile_w, cap, dtype, device), max_ovf,
+                   torch.empty(T, dtype=torch.int32, device=device),
+                   torch.empty(max(max_ovf, 1), dtype=torch.int32, device=device),
+                   torch.empty(1, dtype=torch.int32, device=device),
+                   torch.empty((max(max_ovf, 1), F), dtype=dtype, device=device))
+
+    def desc(self) -> TwellHybridT:
+        return TwellHybridT(self.ell.desc(), self.max_ovf, 0, _ptr(self.row_ovf), _ptr(self.ovf_rows),
+                            _ptr(self.n_ovf), _ptr(self.dense))
+
+
+# ---------------------------------------------------------------- the C entry points
+def twell_pack_gate(x, wg_t, tw: TwELL, stream=None):
+    lib = load()
+    d = ctypes.byref(tw.desc())
+    _check("twell_pack_gate", lib.twell_pack_gate(_ptr(x), _ptr(wg_t), int(x.shape[1]), d, _stream(stream)))
+
+
+def twell_partition_overflow(x, wg_t, hy: Hybrid, stream=None):
+    lib = load()
+    _check("twell_partition_overflow",
+           lib.twell_partition_overflow(_ptr(x), _ptr(wg_t), int(x.shape[1]), ctypes.byref(hy.desc()),
+                                        _stream(stream)))
+
+
+def twell_pack_gate_hybrid(x, wg_t, hy: Hybrid, stream=None):
+    lib = load()
+    _check("twell_pack_gate_hybrid",
+           lib.twell_pack_gate_hybrid(_ptr(x), _ptr(wg_t), int(x.shape[1]), ctypes.byref(hy.desc()),
+                                      _stream(stream)))
+
+
+def twell_ffn_fused(tw: TwELL, x, wu_t, wd, y, stream=None):
+    lib = load()
+    _check("twell_ffn_fused", lib.twell_ffn_fused(ctypes.byref(tw.desc()), _ptr(x), _ptr(wu_t), _ptr(wd),
+                                                  int(x.shape[1]), _ptr(y), _stream(stream)))
+
+
+def twell_ffn_hybrid_workspace_bytes(max_ovf: int, F: int, d: int, dtype) -> int:
+    return int(load().twell_ffn_hybrid_workspace_bytes(max_ovf, F, d, vdtype_of(dtype)))
+
+
+def twell_ffn_hybrid(hy: Hybrid, x, wu_t, wd, y, workspace, stream=None):
+    lib = load()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("twell_ffn_hybrid",
+           lib.twell_ffn_hybrid(ctypes.byref(hy.desc()), _ptr(x), _ptr(wu_t), _ptr(wd), int(x.shape[1]),
+                                _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def twell_ffn_overflow(hy: Hybrid, x, wu_t, wd, y, workspace, stream=None):
+    lib = load()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("twell_ffn_overflow",
+           lib.twell_ffn_overflow(ctypes.byref(hy.desc()), _ptr(x), _ptr(wu_t), _ptr(wd), int(x.shape[1]),
+                                  _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def hybrid_workspace(max_ovf: int, F: int, d: int, dtype, device="cuda"):
+    """A workspace tensor of the size twell_ffn_hybrid needs (256-byte aligned by the allocator)."""
+    import torch
+    n = twell_ffn_hybrid_workspace_bytes(max_ovf, F, d, dtype)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

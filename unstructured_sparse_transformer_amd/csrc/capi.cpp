@@ -1,0 +1,236 @@
+// capi.cpp -- the C ABI declared in include/twell.h: argument checks on the
+// host, then launches on the caller's stream.  Nothing here allocates,
+// synchronises or keeps state between calls.
+#include "twell.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int32_t vdtype) { return vdtype == TWELL_BF16 ? 2 : 4; }
+
+// Shape / type rules shared by every call.
+int check_layout(const twell_t *h, int32_t d)
+{
+    if (!h)
+        return TWELL_E_NULL;
+    if (h->vdtype != TWELL_F32 && h->vdtype != TWELL_BF16)
+        return TWELL_E_UNSUPPORTED;
+    const int w = h->tile_w;
+    if (w != 32 && w != 64 && w != 128 && w != 256)
+        return TWELL_E_UNSUPPORTED;
+    if (h->cap < 1 || h->cap > w)
+        return TWELL_E_UNSUPPORTED;
+    if (h->T < 0 || h->F <= 0 || h->F % w != 0 || h->F % 64 != 0 || d <= 0 || d % 64 != 0)
+        return TWELL_E_SHAPE;
+    // The fused step keeps a token's row in registers: at most 8 KiB per row.
+    if ((int64_t)d * elem_size(h->vdtype) > 8192)
+        return TWELL_E_UNSUPPORTED;
+    return TWELL_OK;
+}
+
+int check_ptrs(const twell_t *h)
+{
+    if (!h->val || !h->idx || !h->cnt)
+        return TWELL_E_NULL;
+    // val / idx / cnt are addressed element-wise; natural alignment suffices.
+    if ((reinterpret_cast<uintptr_t>(h->val) & (elem_size(h->vdtype) - 1)) != 0 ||
+        (reinterpret_cast<uintptr_t>(h->cnt) & 3u) != 0)
+        return TWELL_E_ALIGN;
+    return TWELL_OK;
+}
+
+int check_mat(const void *p)
+{
+    if (!p)
+        return TWELL_E_NULL;
+    return aligned16(p) ? TWELL_OK : TWELL_E_ALIGN;
+}
+
+int check_hybrid(const twell_hybrid_t *hy)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    if (hy->max_ovf < 0)
+        return TWELL_E_SHAPE;
+    if (hy->ell.T == 0)
+        return TWELL_OK;
+    if (!hy->row_ovf || !hy->n_ovf)
+        return TWELL_E_NULL;
+    if (hy->max_ovf > 0 && (!hy->ovf_rows || !hy->dense))
+        return TWELL_E_NULL;
+    if (hy->max_ovf > 0 && !aligned16(hy->dense))
+        return TWELL_E_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(hy->row_ovf) & 3u) || (reinterpret_cast<uintptr_t>(hy->ovf_rows) & 3u) ||
+        (reinterpret_cast<uintptr_t>(hy->n_ovf) & 3u))
+        return TWELL_E_ALIGN;
+    return TWELL_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_E_HIP; }
+
+#define TWELL_TRY(expr)                  \
+    do {                                 \
+        const int _st = (expr);          \
+        if (_st != TWELL_OK)             \
+            return _st;                  \
+    } while (0)
+
+size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
+{
+    const size_t b = (size_t)max_ovf * (size_t)F * (size_t)elem_size(vdtype);
+    return (b + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+int twell_version(void) { return 100; }
+
+const char *twell_status_str(int status)
+{
+    switch (status) {
+    case TWELL_OK:
+        return "ok";
+    case TWELL_E_NULL:
+        return "a required pointer is NULL";
+    case TWELL_E_ALIGN:
+        return "a device pointer is not suitably aligned (16 bytes for x, weights, y, dense)";
+    case TWELL_E_SHAPE:
+        return "bad shape (need T >= 0, d % 64 == 0, F % tile_w == 0, F % 64 == 0)";
+    case TWELL_E_UNSUPPORTED:
+        return "unsupported tile width / capacity / dtype / model width";
+    case TWELL_E_HIP:
+        return "HIP launch failed";
+    case TWELL_E_WORKSPACE:
+        return "workspace missing or too small";
+    default:
+        return "unknown status";
+    }
+}
+
+int twell_pack_gate(const void *x, const void *wg_t, int32_t d, const twell_t *h, void *stream)
+{
+    TWELL_TRY(check_layout(h, d));
+    if (h->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wg_t));
+    TWELL_TRY(check_ptrs(h));
+    return hip_status(twell::launch_gate_twell(h->vdtype, x, wg_t, h->T, d, h->F, h->tile_w, h->cap, h->val, h->idx,
+                                               h->cnt, static_cast<hipStream_t>(stream)));
+}
+
+int twell_partition_overflow(const void *x, const void *wg_t, int32_t d, const twell_hybrid_t *hy, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *h = &hy->ell;
+    TWELL_TRY(check_layout(h, d));
+    TWELL_TRY(check_hybrid(hy));
+    if (h->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wg_t));
+    if (!h->cnt)
+        return TWELL_E_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int n_b = h->F / h->tile_w;
+    TWELL_TRY(hip_status(twell::launch_row_flags(h->cnt, h->T, n_b, h->cap, hy->row_ovf, s)));
+    TWELL_TRY(hip_status(twell::launch_compact_rows(hy->row_ovf, h->T, hy->max_ovf, hy->ovf_rows, hy->n_ovf, s)));
+    return hip_status(twell::launch_dense_gate(h->vdtype, x, wg_t, hy->ovf_rows, hy->n_ovf, hy->max_ovf, d, h->F,
+                                               hy->dense, s));
+}
+
+int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d, const twell_hybrid_t *hy, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    TWELL_TRY(check_layout(&hy->ell, d));
+    TWELL_TRY(check_hybrid(hy));
+    TWELL_TRY(twell_pack_gate(x, wg_t, d, &hy->ell, stream));
+    return twell_partition_overflow(x, wg_t, d, hy, stream);
+}
+
+int twell_ffn_fused(const twell_t *h, const void *x, const void *wu_t, const void *wd, int32_t d, float *y,
+                    void *stream)
+{
+    TWELL_TRY(check_layout(h, d));
+    if (h->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_ptrs(h));
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wu_t));
+    TWELL_TRY(check_mat(wd));
+    TWELL_TRY(check_mat(y));
+    return hip_status(twell::launch_ffn_fused(h->vdtype, h->cnt, h->val, h->idx, h->T, h->F, h->tile_w, h->cap, x,
+                                              wu_t, wd, d, y, static_cast<hipStream_t>(stream)));
+}
+
+size_t twell_ffn_hybrid_workspace_bytes(int32_t max_ovf, int32_t F, int32_t d, int32_t vdtype)
+{
+    if (max_ovf <= 0 || F <= 0 || d <= 0)
+        return 0;
+    const int splits = twell::down_splits(max_ovf, F, d);
+    size_t b = hybrid_ws_p_bytes(max_ovf, F, vdtype);
+    if (splits > 1)
+        b += (size_t)splits * (size_t)max_ovf * (size_t)d * sizeof(float);
+    return b;
+}
+
+int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd, int32_t d,
+                       float *y, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *h = &hy->ell;
+    TWELL_TRY(check_layout(h, d));
+    TWELL_TRY(check_hybrid(hy));
+    if (h->T == 0 || hy->max_ovf == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wu_t));
+    TWELL_TRY(check_mat(wd));
+    TWELL_TRY(check_mat(y));
+    const size_t need = twell_ffn_hybrid_workspace_bytes(hy->max_ovf, h->F, d, h->vdtype);
+    if (!workspace || workspace_bytes < need)
+        return TWELL_E_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return TWELL_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *pbuf = ws;
+    const int splits = twell::down_splits(hy->max_ovf, h->F, d);
+    float *part = splits > 1 ? reinterpret_cast<float *>(ws + hybrid_ws_p_bytes(hy->max_ovf, h->F, h->vdtype))
+                             : nullptr;
+    TWELL_TRY(hip_status(twell::launch_gated_up(h->vdtype, x, wu_t, hy->ovf_rows, hy->n_ovf, hy->max_ovf, d, h->F,
+                                                hy->dense, pbuf, s)));
+    return hip_status(twell::launch_down(h->vdtype, pbuf, wd, hy->ovf_rows, hy->n_ovf, hy->max_ovf, h->F, d, y, part,
+                                         splits, s));
+}
+
+int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd, int32_t d, float *y,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *h = &hy->ell;
+    TWELL_TRY(check_layout(h, d));
+    TWELL_TRY(check_hybrid(hy));
+    if (h->T == 0)
+        return TWELL_OK;
+    const size_t need = twell_ffn_hybrid_workspace_bytes(hy->max_ovf, h->F, d, h->vdtype);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return TWELL_E_WORKSPACE;
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return TWELL_E_ALIGN;
+    TWELL_TRY(twell_ffn_fused(h, x, wu_t, wd, d, y, stream));
+    return twell_ffn_overflow(hy, x, wu_t, wd, d, y, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

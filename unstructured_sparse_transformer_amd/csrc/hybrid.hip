@@ -1,0 +1,285 @@
+// hybrid.hip -- the ELL + dense-backup hybrid ("Sparser, Faster, Lighter
+// Transformer Language Models", gist.science summary, section 2.3): rows whose
+// nonzeros overflow the fixed ELL capacity are moved to a dense backup matrix,
+// the rest stay in the compact ELL part; the partition is dynamic.
+//
+// Steps on the device, all on the caller's stream with no host round trip:
+//   row_flags     row_ovf[t] = some tile of row t has cnt > cap
+//   compact_rows  one workgroup turns the flags into the ascending overflow-row
+//                 list and its length (ballot + popcount prefix, no atomics)
+//   dense_gate    ReLU(x . W_g) for the listed rows  -> dense backup
+//   gated_up      round(dense * (x . W_u))  for the listed rows -> workspace
+//   down          (gated product) . W_d     -> y rows of the listed tokens
+// The three GEMMs run with M = min(n_ovf, max_ovf) read on the device:
+// workgroups past it return at once.
+#include "launch.h"
+#include "twell_device.h"
+
+namespace twell {
+
+// ------------------------------------------------------------------ partition
+__global__ __launch_bounds__(256) void row_flags_kernel(const int32_t *__restrict__ cnt, int T, int n_b, int cap,
+                                                        int32_t *__restrict__ row_ovf)
+{
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T)
+        return;
+    const int32_t *c = cnt + (int64_t)t * n_b;
+    int f = 0;
+    for (int b = 0; b < n_b; ++b)
+        f |= c[b] > cap;
+    row_ovf[t] = f;
+}
+
+__global__ __launch_bounds__(1024) void compact_rows_kernel(const int32_t *__restrict__ row_ovf, int T, int max_ovf,
+                                                            int32_t *__restrict__ ovf_rows,
+                                                            int32_t *__restrict__ n_ovf)
+{
+    __shared__ int wave_tot[16];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint64_t lower = lane ? (~0ull >> (64 - lane)) : 0ull;
+    int base = 0;
+    for (int t0 = 0; t0 < T; t0 += 1024) {
+        const int t = t0 + tid;
+        const bool f = t < T && row_ovf[t] != 0;
+        const uint64_t m = __ballot(f);
+        if (lane == 0)
+            wave_tot[wave] = __popcll(m);
+        __syncthreads();
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int c = wave_tot[w];
+            off += w < wave ? c : 0;
+            tot += c;
+        }
+        const int pos = base + off + __popcll(m & lower);
+        if (f && pos < max_ovf)
+            ovf_rows[pos] = t;
+        base += tot;
+        __syncthreads();
+    }
+    if (tid == 0)
+        n_ovf[0] = base;
+}
+
+hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, hipStream_t s)
+{
+    row_flags_kernel<<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, T, n_b, cap, row_ovf);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows, int32_t *n_ovf,
+                               hipStream_t s)
+{
+    compact_rows_kernel<<<dim3(1), dim3(1024), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ dense GEMMs
+template <typename TI> struct DenseOut {
+    TI *out;            // [max_ovf][N]
+    const TI *gate;     // MODE 1: dense backup [max_ovf][N]
+};
+
+__device__ __forceinline__ int rows_used(const GemmArgs &p)
+{
+    const int n = *p.m_count;
+    return n < p.M ? n : p.M;
+}
+
+// MODE 0: out = ReLU(acc) (dense backup).  MODE 1: out = round(gate * acc).
+template <typename TI, int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dense_epi_kernel(GemmArgs p, DenseOut<TI> o)
+{
+    using Core = GemmCore<TI, BM, BN, WM, WN, false>;
+    __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
+    const int m_used = rows_used(p);
+    int mt, nt;
+    tile_coords(blockIdx.x, p.MT, p.NT, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    if (m0 >= m_used)
+        return;
+    Core core;
+    f32x16 acc[Core::FM][Core::FN];
+    core.run(p, smem, m0, n0, m_used, p.k_begin, p.k_len, threadIdx.x, acc);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / Core::NWN, wn = wave % Core::NWN;
+#pragma unroll
+    for (int fm = 0; fm < Core::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Core::FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
+                const int n = n0 + wn * WN + fn * 32 + (lane & 31);
+                if (m < m_used && n < p.N) {
+                    const int64_t off = (int64_t)m * p.N + n;
+                    const float v = acc[fm][fn][i];
+                    if (MODE == 0)
+                        store_elem(o.out + off, v > 0.f ? v : 0.f);
+                    else
+                        store_elem(o.out + off, load_elem(o.gate + off) * v);
+                }
+            }
+}
+
+template <typename TI> struct DownOut {
+    float *part;           // [splits][M][N] when splits > 1
+    float *y;              // [*][N]
+    const int32_t *rows;   // output row of local row m
+    int splits;
+};
+
+template <typename TI, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void down_kernel(GemmArgs p, DownOut<TI> o)
+{
+    using Core = GemmCore<TI, BM, BN, WM, WN, true>;
+    __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
+    const int m_used = rows_used(p);
+    int mt, nt;
+    tile_coords(blockIdx.x, p.MT, p.NT, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    if (m0 >= m_used)
+        return;
+    const int sidx = blockIdx.y;
+    Core core;
+    f32x16 acc[Core::FM][Core::FN];
+    core.run(p, smem, m0, n0, m_used, p.k_begin + sidx * p.k_split_len, p.k_split_len, threadIdx.x, acc);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / Core::NWN, wn = wave % Core::NWN;
+#pragma unroll
+    for (int fm = 0; fm < Core::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Core::FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
+                const int n = n0 + wn * WN + fn * 32 + (lane & 31);
+                if (m < m_used && n < p.N) {
+                    if (o.splits == 1)
+                        o.y[(int64_t)o.rows[m] * p.N + n] = acc[fm][fn][i];
+                    else
+                        o.part[((int64_t)sidx * p.M + m) * p.N + n] = acc[fm][fn][i];
+                }
+            }
+}
+
+// y[rows[m]][n] = sum over splits s (in order) of part[s][m][n].
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ part, int splits, int M_cap,
+                                                           const int32_t *__restrict__ m_count, int N,
+                                                           const int32_t *__restrict__ rows, float *__restrict__ y)
+{
+    const int mc = *m_count;
+    const int m_used = mc < M_cap ? mc : M_cap;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (n >= N)
+        return;
+    for (int m = blockIdx.y; m < m_used; m += gridDim.y) {
+        float4 acc = *reinterpret_cast<const float4 *>(part + (int64_t)m * N + n);
+        for (int s = 1; s < splits; ++s) {
+            const float4 v = *reinterpret_cast<const float4 *>(part + ((int64_t)s * M_cap + m) * N + n);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        *reinterpret_cast<float4 *>(y + (int64_t)rows[m] * N + n) = acc;
+    }
+}
+
+// Small-M tile shape for the hybrid GEMMs: 64 x 128 per workgroup, 4 waves.
+constexpr int HB_BM = 64, HB_BN = 128, HB_WM = 32, HB_WN = 64;
+
+template <typename TI, int MODE>
+static hipError_t dense_go(const void *x, const void *w_t, const int32_t *ovf_rows, const int32_t *n_ovf,
+                           int max_ovf, int d, int F, const void *gate, void *out, hipStream_t s)
+{
+    if (max_ovf == 0)
+        return hipSuccess;
+    GemmArgs p{};
+    p.A = x;
+    p.lda = d;
+    p.a_rows = ovf_rows;
+    p.M = max_ovf;
+    p.m_count = n_ovf;
+    p.B = w_t;
+    p.ldb = d;
+    p.N = F;
+    p.k_begin = 0;
+    p.k_len = d;
+    p.MT = (max_ovf + HB_BM - 1) / HB_BM;
+    p.NT = (F + HB_BN - 1) / HB_BN;
+    DenseOut<TI> o{static_cast<TI *>(out), static_cast<const TI *>(gate)};
+    dense_epi_kernel<TI, HB_BM, HB_BN, HB_WM, HB_WN, MODE>
+        <<<dim3(p.MT * p.NT), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_gate(int vdtype, const void *x, const void *wg_t, const int32_t *ovf_rows,
+                             const int32_t *n_ovf, int max_ovf, int d, int F, void *dense, hipStream_t s)
+{
+    if (vdtype == 1)
+        return dense_go<__bf16, 0>(x, wg_t, ovf_rows, n_ovf, max_ovf, d, F, nullptr, dense, s);
+    return dense_go<float, 0>(x, wg_t, ovf_rows, n_ovf, max_ovf, d, F, nullptr, dense, s);
+}
+
+hipError_t launch_gated_up(int vdtype, const void *x, const void *wu_t, const int32_t *ovf_rows,
+                           const int32_t *n_ovf, int max_ovf, int d, int F, const void *dense, void *pbuf,
+                           hipStream_t s)
+{
+    if (vdtype == 1)
+        return dense_go<__bf16, 1>(x, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
+    return dense_go<float, 1>(x, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
+}
+
+int down_splits(int max_ovf, int F, int d)
+{
+    // Aim for >= ~512 workgroups when every listed row is used; K slices stay
+    // whole multiples of 64 elements.
+    const long tiles = (long)((max_ovf + HB_BM - 1) / HB_BM) * ((d + HB_BN - 1) / HB_BN);
+    int s = 1;
+    while (s < 8 && tiles * s < 512 && F % (s * 2 * 64) == 0)
+        s *= 2;
+    return s;
+}
+
+template <typename TI>
+static hipError_t down_go(const void *pbuf, const void *wd, const int32_t *ovf_rows, const int32_t *n_ovf,
+                          int max_ovf, int F, int d, float *y, float *part, int splits, hipStream_t s)
+{
+    if (max_ovf == 0)
+        return hipSuccess;
+    GemmArgs p{};
+    p.A = pbuf;
+    p.lda = F;
+    p.M = max_ovf;
+    p.m_count = n_ovf;
+    p.B = wd;
+    p.ldb = d;
+    p.N = d;
+    p.k_begin = 0;
+    p.k_len = F;
+    p.k_split_len = F / splits;
+    p.MT = (max_ovf + HB_BM - 1) / HB_BM;
+    p.NT = (d + HB_BN - 1) / HB_BN;
+    DownOut<TI> o{part, y, ovf_rows, splits};
+    down_kernel<TI, HB_BM, HB_BN, HB_WM, HB_WN>
+        <<<dim3(p.MT * p.NT, splits), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1)
+        return e;
+    split_reduce_kernel<<<dim3((d / 4 + 255) / 256, max_ovf < 4096 ? max_ovf : 4096), dim3(256), 0, s>>>(part, splits, max_ovf, n_ovf, d,
+                                                                             ovf_rows, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_down(int vdtype, const void *pbuf, const void *wd, const int32_t *ovf_rows, const int32_t *n_ovf,
+                       int max_ovf, int F, int d, float *y, float *part, int splits, hipStream_t s)
+{
+    if (vdtype == 1)
+        return down_go<__bf16>(pbuf, wd, ovf_rows, n_ovf, max_ovf, F, d, y, part, splits, s);
+    return down_go<float>(pbuf, wd, ovf_rows, n_ovf, max_ovf, F, d, y, part, splits, s);
+}
+
+}  // namespace twell

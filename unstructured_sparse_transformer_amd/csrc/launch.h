@@ -1,0 +1,43 @@
+// launch.h -- internal launchers behind the C ABI (host side).  Every
+// launcher assumes the C-ABI layer has validated its arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace twell {
+
+// Gate GEMM + TwELL epilogue over all T rows.
+hipError_t launch_gate_twell(int vdtype, const void *x, const void *wg_t, int T, int d, int F, int tile_w,
+                             int cap, void *val, uint8_t *idx, int32_t *cnt, hipStream_t s);
+
+// row_ovf[t] = any tile of row t has cnt > cap.
+hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, hipStream_t s);
+
+// Ascending list of flagged rows (first max_ovf of them) and their total count.
+hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows, int32_t *n_ovf,
+                               hipStream_t s);
+
+// dense[i][:] = ReLU(x[ovf_rows[i]] . W_g) for i < min(*n_ovf, max_ovf).
+hipError_t launch_dense_gate(int vdtype, const void *x, const void *wg_t, const int32_t *ovf_rows,
+                             const int32_t *n_ovf, int max_ovf, int d, int F, void *dense, hipStream_t s);
+
+// p[i][:] = round(dense[i][:] * (x[ovf_rows[i]] . W_u)) for i < min(*n_ovf, max_ovf).
+hipError_t launch_gated_up(int vdtype, const void *x, const void *wu_t, const int32_t *ovf_rows,
+                           const int32_t *n_ovf, int max_ovf, int d, int F, const void *dense, void *p,
+                           hipStream_t s);
+
+// y[ovf_rows[i]][:] = p[i][:] . W_d for i < min(*n_ovf, max_ovf); split-K with
+// `splits` fp32 partial slabs in `part` ([splits][max_ovf][d]) when splits > 1.
+hipError_t launch_down(int vdtype, const void *p, const void *wd, const int32_t *ovf_rows, const int32_t *n_ovf,
+                       int max_ovf, int F, int d, float *y, float *part, int splits, hipStream_t s);
+
+// Fused up/down from TwELL for every row (overflow rows -> 0).
+hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F,
+                            int tile_w, int cap, const void *x, const void *wu_t, const void *wd, int d, float *y,
+                            hipStream_t s);
+
+// Number of split-K slabs the hybrid down projection uses for these sizes.
+int down_splits(int max_ovf, int F, int d);
+
+}  // namespace twell
