@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run a plain 256 MiB device copy 3x first (counter calibration under rocprofv3)")
     return ap.parse_args()
 
 
@@ -81,6 +83,15 @@ def main():
     ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt)
     y = torch.empty((wl.T, wl.d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+
+    if args.calib_copy:
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x (268435456 B read + 268435456 B written)")
+        del src, dst
 
     def step(ev=None):
         if ev:

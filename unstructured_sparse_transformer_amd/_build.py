@@ -27,6 +27,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     # no packed-fp32 (v_pk_*_f32) code generation
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the epilogues fully unroll over all accumulator registers (no dynamic
+    # indexing -> no scratch); allow the unroller the size that needs
+    "-mllvm", "-pragma-unroll-threshold=65536",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -30,6 +30,10 @@ int check_layout(const twell_t *h, int32_t d)
     // The fused step keeps a token's row in registers: at most 8 KiB per row.
     if ((int64_t)d * elem_size(h->vdtype) > 8192)
         return TWELL_E_UNSUPPORTED;
+    // GEMM operands are addressed with 32-bit byte offsets: each matrix < 4 GiB.
+    const int64_t lim = (int64_t)1 << 32;
+    if ((int64_t)h->T * d * elem_size(h->vdtype) >= lim || (int64_t)h->F * d * elem_size(h->vdtype) >= lim)
+        return TWELL_E_SHAPE;
     return TWELL_OK;
 }
 
@@ -55,7 +59,7 @@ int check_hybrid(const twell_hybrid_t *hy)
 {
     if (!hy)
         return TWELL_E_NULL;
-    if (hy->max_ovf < 0)
+    if (hy->max_ovf < 0 || (int64_t)hy->max_ovf * hy->ell.F * elem_size(hy->ell.vdtype) >= ((int64_t)1 << 32))
         return TWELL_E_SHAPE;
     if (hy->ell.T == 0)
         return TWELL_OK;
@@ -143,7 +147,7 @@ int twell_partition_overflow(const void *x, const void *wg_t, int32_t d, const t
     const int n_b = h->F / h->tile_w;
     TWELL_TRY(hip_status(twell::launch_row_flags(h->cnt, h->T, n_b, h->cap, hy->row_ovf, s)));
     TWELL_TRY(hip_status(twell::launch_compact_rows(hy->row_ovf, h->T, hy->max_ovf, hy->ovf_rows, hy->n_ovf, s)));
-    return hip_status(twell::launch_dense_gate(h->vdtype, x, wg_t, hy->ovf_rows, hy->n_ovf, hy->max_ovf, d, h->F,
+    return hip_status(twell::launch_dense_gate(h->vdtype, x, h->T, wg_t, hy->ovf_rows, hy->n_ovf, hy->max_ovf, d, h->F,
                                                hy->dense, s));
 }
 
@@ -208,7 +212,7 @@ int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const void *wu_t
     const int splits = twell::down_splits(hy->max_ovf, h->F, d);
     float *part = splits > 1 ? reinterpret_cast<float *>(ws + hybrid_ws_p_bytes(hy->max_ovf, h->F, h->vdtype))
                              : nullptr;
-    TWELL_TRY(hip_status(twell::launch_gated_up(h->vdtype, x, wu_t, hy->ovf_rows, hy->n_ovf, hy->max_ovf, d, h->F,
+    TWELL_TRY(hip_status(twell::launch_gated_up(h->vdtype, x, h->T, wu_t, hy->ovf_rows, hy->n_ovf, hy->max_ovf, d, h->F,
                                                 hy->dense, pbuf, s)));
     return hip_status(twell::launch_down(h->vdtype, pbuf, wd, hy->ovf_rows, hy->n_ovf, hy->max_ovf, h->F, d, y, part,
                                          splits, s));

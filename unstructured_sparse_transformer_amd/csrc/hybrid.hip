@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 constexpr int HB_BM = 64, HB_BN = 128, HB_WM = 32, HB_WN = 64;
 
 template <typename TI, int MODE>
-static hipError_t dense_go(const void *x, const void *w_t, const int32_t *ovf_rows, const int32_t *n_ovf,
+static hipError_t dense_go(const void *x, int T, const void *w_t, const int32_t *ovf_rows, const int32_t *n_ovf,
                            int max_ovf, int d, int F, const void *gate, void *out, hipStream_t s)
 {
     if (max_ovf == 0)
@@ -210,27 +210,29 @@ static hipError_t dense_go(const void *x, const void *w_t, const int32_t *ovf_ro
     p.k_len = d;
     p.MT = (max_ovf + HB_BM - 1) / HB_BM;
     p.NT = (F + HB_BN - 1) / HB_BN;
+    p.a_bytes = (uint32_t)((int64_t)T * d * sizeof(TI));
+    p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
     DenseOut<TI> o{static_cast<TI *>(out), static_cast<const TI *>(gate)};
     dense_epi_kernel<TI, HB_BM, HB_BN, HB_WM, HB_WN, MODE>
         <<<dim3(p.MT * p.NT), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);
     return hipGetLastError();
 }
 
-hipError_t launch_dense_gate(int vdtype, const void *x, const void *wg_t, const int32_t *ovf_rows,
+hipError_t launch_dense_gate(int vdtype, const void *x, int T, const void *wg_t, const int32_t *ovf_rows,
                              const int32_t *n_ovf, int max_ovf, int d, int F, void *dense, hipStream_t s)
 {
     if (vdtype == 1)
-        return dense_go<__bf16, 0>(x, wg_t, ovf_rows, n_ovf, max_ovf, d, F, nullptr, dense, s);
-    return dense_go<float, 0>(x, wg_t, ovf_rows, n_ovf, max_ovf, d, F, nullptr, dense, s);
+        return dense_go<__bf16, 0>(x, T, wg_t, ovf_rows, n_ovf, max_ovf, d, F, nullptr, dense, s);
+    return dense_go<float, 0>(x, T, wg_t, ovf_rows, n_ovf, max_ovf, d, F, nullptr, dense, s);
 }
 
-hipError_t launch_gated_up(int vdtype, const void *x, const void *wu_t, const int32_t *ovf_rows,
+hipError_t launch_gated_up(int vdtype, const void *x, int T, const void *wu_t, const int32_t *ovf_rows,
                            const int32_t *n_ovf, int max_ovf, int d, int F, const void *dense, void *pbuf,
                            hipStream_t s)
 {
     if (vdtype == 1)
-        return dense_go<__bf16, 1>(x, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
-    return dense_go<float, 1>(x, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
+        return dense_go<__bf16, 1>(x, T, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
+    return dense_go<float, 1>(x, T, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
 }
 
 int down_splits(int max_ovf, int F, int d)
@@ -263,6 +265,8 @@ static hipError_t down_go(const void *pbuf, const void *wd, const int32_t *ovf_r
     p.k_split_len = F / splits;
     p.MT = (max_ovf + HB_BM - 1) / HB_BM;
     p.NT = (d + HB_BN - 1) / HB_BN;
+    p.a_bytes = (uint32_t)((int64_t)max_ovf * F * sizeof(TI));
+    p.b_bytes = 0;  // KN-layout B is read through plain pointers
     DownOut<TI> o{part, y, ovf_rows, splits};
     down_kernel<TI, HB_BM, HB_BN, HB_WM, HB_WN>
         <<<dim3(p.MT * p.NT, splits), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);

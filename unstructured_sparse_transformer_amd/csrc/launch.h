@@ -19,11 +19,11 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
                                hipStream_t s);
 
 // dense[i][:] = ReLU(x[ovf_rows[i]] . W_g) for i < min(*n_ovf, max_ovf).
-hipError_t launch_dense_gate(int vdtype, const void *x, const void *wg_t, const int32_t *ovf_rows,
+hipError_t launch_dense_gate(int vdtype, const void *x, int T, const void *wg_t, const int32_t *ovf_rows,
                              const int32_t *n_ovf, int max_ovf, int d, int F, void *dense, hipStream_t s);
 
 // p[i][:] = round(dense[i][:] * (x[ovf_rows[i]] . W_u)) for i < min(*n_ovf, max_ovf).
-hipError_t launch_gated_up(int vdtype, const void *x, const void *wu_t, const int32_t *ovf_rows,
+hipError_t launch_gated_up(int vdtype, const void *x, int T, const void *wu_t, const int32_t *ovf_rows,
                            const int32_t *n_ovf, int max_ovf, int d, int F, const void *dense, void *p,
                            hipStream_t s);
 

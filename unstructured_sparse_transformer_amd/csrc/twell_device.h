@@ -1,9 +1,10 @@
 // twell_device.h -- device-side building blocks of libtwell (gfx950 only).
 //
 // * 16-byte "chunk" loads and a swizzled LDS tile layout shared by every GEMM:
-//   a tile row holds 128 bytes of the K dimension (64 bf16 or 32 fp32) as 8
-//   chunks; chunk c of row r lives at chunk slot c ^ (r & 7), so the 32 rows a
-//   half-wave reads for one MFMA operand hit 8 distinct 16-byte bank groups.
+//   a tile row holds KB bytes of the K dimension (KB = 128: 64 bf16 / 32 fp32,
+//   or KB = 64) as KB/16 chunks, XOR-swizzled per row (see lds_off) so that
+//   16 consecutive rows read at one logical chunk hit 16 distinct 16-byte
+//   bank groups, and a 1 KiB global->LDS copy (whole rows) does too.
 // * MFMA step on one chunk per lane: bf16 -> one v_mfma_f32_32x32x16_bf16;
 //   fp32 -> four v_mfma_f32_32x32x2f32.  Lanes 0-31 supply chunk 2s and lanes
 //   32-63 chunk 2s+1 of the same rows; A and B use the same K mapping, so the
@@ -53,7 +54,17 @@ __device__ __forceinline__ float round_to_elem(float, float v) { return v; }
 
 __device__ __forceinline__ u32x4 ldg16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return (row << 7) + ((chunk ^ (row & 7)) << 4); }
+// Byte offset of logical chunk `chunk` of tile row `row` in an LDS tile whose
+// rows hold KB bytes (KB/16 chunks).  A 256-byte bank window holds 256/KB
+// rows; the chunk slot is XORed with the row's index among the rows that share
+// a window position, so 16 consecutive rows read at one logical chunk (one
+// 16-lane phase of ds_read_b128) hit 16 distinct 16-byte bank groups.
+template <int KB> __device__ __forceinline__ int lds_off(int row, int chunk)
+{
+    constexpr int CPR = KB / 16;        // chunks per row
+    constexpr int RPW_LOG = KB == 128 ? 1 : 2;  // log2(rows per 256-byte window)
+    return row * KB + ((chunk ^ ((row >> RPW_LOG) & (CPR - 1))) << 4);
+}
 
 __device__ __forceinline__ void mfma_chunk(__bf16, const u32x4 &a, const u32x4 &b, f32x16 &acc)
 {
@@ -108,58 +119,92 @@ struct GemmArgs {
     int k_begin, k_len;      // elements; k_len multiple of the 128-byte K tile
     int k_split_len;         // split-K: workgroup z-slice s covers [k_begin + s*k_split_len, +k_split_len)
     int MT, NT;              // tile grid
+    uint32_t a_bytes, b_bytes;  // extents of A and B (each below 4 GiB)
 };
 
-template <typename TI, int BM, int BN, int WM, int WN, bool B_KN>
+// Buffer resource over one matrix (raw, stride 0): word 3 as CDNA3/CDNA4
+// expect for untyped dword loads.  `bytes` is the extent of the matrix.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes LDS bytes [dst + 16 l, dst + 16 l + 16).  No VGPRs hold the data.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *dst, int voff, int soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including the
+// global->LDS copies) and LDS operations have completed (vmcnt = lgkmcnt = 0).
+__device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+template <typename TI, int BM, int BN, int WM, int WN, bool B_KN, int KB = 128, int STAGES = 2>
 struct GemmCore {
     static constexpr int NWM = BM / WM, NWN = BN / WN;
-    static constexpr int NTHR = NWM * NWN * 64;
+    static constexpr int NW = NWM * NWN;
+    static constexpr int NTHR = NW * 64;
     static constexpr int FM = WM / 32, FN = WN / 32;
     static constexpr int E = Elt<TI>::PER_CHUNK;
-    static constexpr int KT = 128 / Elt<TI>::SIZE;      // K elements per tile
-    static constexpr int A_CH = BM * 8 / NTHR;          // A chunks per thread per tile
-    static constexpr int B_CH = B_KN ? 0 : BN * 8 / NTHR;
-    static constexpr int B_UNITS = B_KN ? 8 * BN / E : 0;  // E x E transpose units per tile
+    static constexpr int SZ = Elt<TI>::SIZE;
+    static constexpr int CPR = KB / 16;                  // chunks per tile row
+    static constexpr int KT = KB / SZ;                   // K elements per stage
+    static constexpr int SUB = KB / 32;                  // MFMA sub-steps per stage
+    static constexpr int RPC = 1024 / KB;                // tile rows per 1 KiB copy
+    // K-contiguous operands arrive by global->LDS copies of 1 KiB per wave
+    // instruction (RPC whole tile rows).
+    static constexpr int A_LD = BM / RPC / NW;
+    static constexpr int B_LD = B_KN ? 0 : BN / RPC / NW;
+    static constexpr int B_UNITS = B_KN ? CPR * BN / E : 0;  // E x E transpose units per stage
     static constexpr int B_UPT = B_KN ? (B_UNITS + NTHR - 1) / NTHR : 0;
-    static constexpr int LDS_A = BM * 128, LDS_B = BN * 128;
-    static constexpr int LDS_BYTES = 2 * (LDS_A + LDS_B);
-    static_assert(BM * 8 % NTHR == 0, "A tile load split");
-    static_assert(B_KN || (BN * 8 % NTHR == 0), "B tile load split");
+    static constexpr int LDS_A = BM * KB, LDS_B = BN * KB;
+    static constexpr int BUF = LDS_A + LDS_B;
+    static constexpr int LDS_BYTES = STAGES * BUF;
+    static_assert(KB == 64 || KB == 128, "stage row width");
+    static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+    static_assert(!B_KN || STAGES == 2, "the register-transposed B path is double-buffered only");
+    static_assert((BM / RPC) % NW == 0, "A tile rows split over the waves");
+    static_assert(B_KN || (BN / RPC) % NW == 0, "B tile rows split over the waves");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is whole 32x32 blocks");
 
-    const char *a_ptr[A_CH];
-    int a_lds[A_CH];
-    const char *b_ptr[B_KN ? 1 : B_CH];
-    int b_lds[B_KN ? 1 : B_CH];
-    u32x4 a_reg[A_CH];
-    u32x4 b_reg[B_KN ? (B_UPT * E) : B_CH];
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int a_voff[A_LD];
+    int b_voff[B_LD > 0 ? B_LD : 1];
+    u32x4 b_reg[B_KN ? (B_UPT * E) : 1];
     const char *bkn_ptr[B_KN ? B_UPT : 1];
     int bkn_row0[B_KN ? B_UPT : 1], bkn_chunk[B_KN ? B_UPT : 1];
     bool bkn_on[B_KN ? B_UPT : 1];
     int64_t ldb_bytes;
+    int wave;
 
+    // Lane l of copy j of this wave fills tile row g*RPC + l/CPR (g = j*NW + wave)
+    // at physical chunk slot l%CPR, i.e. it loads the logical chunk that the
+    // swizzle maps to that slot.
     __device__ __forceinline__ void setup(const GemmArgs &p, int m0, int n0, int m_used, int kb, int tid)
     {
-        constexpr int SZ = Elt<TI>::SIZE;
+        wave = tid >> 6;
+        const int lane = tid & 63;
+        constexpr int RPW_LOG = KB == 128 ? 1 : 2;
+        ra = make_rsrc(p.A, p.a_bytes);
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int q = tid + i * NTHR;
-            const int r = q >> 3, c = q & 7;
+        for (int j = 0; j < A_LD; ++j) {
+            const int r = (j * NW + wave) * RPC + lane / CPR;
+            const int c = (lane % CPR) ^ ((r >> RPW_LOG) & (CPR - 1));
             int gm = m0 + r;
-            gm = gm < m_used ? gm : m_used - 1;  // rows past the end read a valid row; results discarded
+            gm = gm < m_used ? gm : m_used - 1;  // rows past the end re-read a valid row; results discarded
             const int64_t ar = p.a_rows ? (int64_t)p.a_rows[gm] : (int64_t)gm;
-            a_ptr[i] = (const char *)p.A + (ar * p.lda + kb) * SZ + c * 16;
-            a_lds[i] = lds_off(r, c);
+            a_voff[j] = (int)((ar * p.lda + kb) * SZ + c * 16);
         }
         if constexpr (!B_KN) {
+            rb = make_rsrc(p.B, p.b_bytes);
 #pragma unroll
-            for (int i = 0; i < B_CH; ++i) {
-                const int q = tid + i * NTHR;
-                const int r = q >> 3, c = q & 7;
+            for (int j = 0; j < B_LD; ++j) {
+                const int r = (j * NW + wave) * RPC + lane / CPR;
+                const int c = (lane % CPR) ^ ((r >> RPW_LOG) & (CPR - 1));
                 int gn = n0 + r;
                 gn = gn < p.N ? gn : p.N - 1;
-                b_ptr[i] = (const char *)p.B + ((int64_t)gn * p.ldb + kb) * SZ + c * 16;
-                b_lds[i] = lds_off(r, c);
+                b_voff[j] = (int)(((int64_t)gn * p.ldb + kb) * SZ + c * 16);
             }
         } else {
             ldb_bytes = p.ldb * SZ;
@@ -167,7 +212,7 @@ struct GemmCore {
             for (int i = 0; i < B_UPT; ++i) {
                 const int u = tid + i * NTHR;
                 bkn_on[i] = u < B_UNITS;
-                const int kg = u & 7, ng = u >> 3;  // k group (chunk within the K tile), n group
+                const int kg = u % CPR, ng = u / CPR;  // k group (chunk within the stage), n group
                 int gn = n0 + ng * E;
                 gn = gn <= p.N - E ? gn : p.N - E;
                 bkn_ptr[i] = (const char *)p.B + ((int64_t)(kb + kg * E) * p.ldb + gn) * SZ;
@@ -177,16 +222,18 @@ struct GemmCore {
         }
     }
 
-    __device__ __forceinline__ void load(int kt)
+    // Queue stage kt's global->LDS copies into buffer `buf`; KN-layout B goes to registers.
+    __device__ __forceinline__ void load(int kt, char *buf)
     {
-        const int64_t koff = (int64_t)kt * 128;
+        const int koff = kt * KB;
+        char *sa = buf, *sb = buf + LDS_A;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i)
-            a_reg[i] = ldg16(a_ptr[i] + koff);
+        for (int j = 0; j < A_LD; ++j)
+            dma16(ra, sa + (j * NW + wave) * 1024, a_voff[j], koff);
         if constexpr (!B_KN) {
 #pragma unroll
-            for (int i = 0; i < B_CH; ++i)
-                b_reg[i] = ldg16(b_ptr[i] + koff);
+            for (int j = 0; j < B_LD; ++j)
+                dma16(rb, sb + (j * NW + wave) * 1024, b_voff[j], koff);
         } else {
             const int64_t krow = (int64_t)kt * KT * ldb_bytes;
 #pragma unroll
@@ -199,25 +246,19 @@ struct GemmCore {
         }
     }
 
-    __device__ __forceinline__ void store(char *sa, char *sb)
+    // KN-layout B: registers -> LDS, transposed so each column's K run is one chunk.
+    __device__ __forceinline__ void store_b(char *buf)
     {
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i)
-            *reinterpret_cast<u32x4 *>(sa + a_lds[i]) = a_reg[i];
-        if constexpr (!B_KN) {
-#pragma unroll
-            for (int i = 0; i < B_CH; ++i)
-                *reinterpret_cast<u32x4 *>(sb + b_lds[i]) = b_reg[i];
-        } else {
+        if constexpr (B_KN) {
+            char *sb = buf + LDS_A;
 #pragma unroll
             for (int i = 0; i < B_UPT; ++i)
                 if (bkn_on[i]) {
-                    // b_reg[i*E + e] holds row k = e, columns n = 0..E-1; LDS wants, for
-                    // each column n, the E k-values as one chunk.
+                    // b_reg[i*E + e] holds row k = e, columns n = 0..E-1
 #pragma unroll
                     for (int n = 0; n < E; ++n) {
                         u32x4 o;
-                        if constexpr (Elt<TI>::SIZE == 2) {
+                        if constexpr (SZ == 2) {
 #pragma unroll
                             for (int w = 0; w < 4; ++w) {
                                 const uint32_t lo = b_reg[i * E + 2 * w][n >> 1];
@@ -231,40 +272,69 @@ struct GemmCore {
                             for (int w = 0; w < 4; ++w)
                                 o[w] = b_reg[i * E + w][n];
                         }
-                        *reinterpret_cast<u32x4 *>(sb + lds_off(bkn_row0[i] + n, bkn_chunk[i])) = o;
+                        *reinterpret_cast<u32x4 *>(sb + lds_off<KB>(bkn_row0[i] + n, bkn_chunk[i])) = o;
                     }
                 }
         }
     }
 
-    __device__ __forceinline__ void compute(const char *sa, const char *sb, int wm, int wn, int lane,
-                                            f32x16 (&acc)[FM][FN])
+    // The MFMA sub-steps of one stage; fragments of sub-step s+1 are read from
+    // LDS while the MFMAs of sub-step s run.
+    __device__ __forceinline__ void compute(const char *buf, int wm, int wn, int lane, f32x16 (&acc)[FM][FN])
     {
+        const char *sa = buf, *sb = buf + LDS_A;
         const int lr = lane & 31, lh = lane >> 5;
+        u32x4 af[2][FM], bfr[2][FN];
 #pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-            u32x4 af[FM], bfr[FN];
+        for (int fm = 0; fm < FM; ++fm)
+            af[0][fm] = *reinterpret_cast<const u32x4 *>(sa + lds_off<KB>(wm * WM + fm * 32 + lr, lh));
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-                af[fm] = *reinterpret_cast<const u32x4 *>(sa + lds_off(wm * WM + fm * 32 + lr, ss * 2 + lh));
+        for (int fn = 0; fn < FN; ++fn)
+            bfr[0][fn] = *reinterpret_cast<const u32x4 *>(sb + lds_off<KB>(wn * WN + fn * 32 + lr, lh));
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                bfr[fn] = *reinterpret_cast<const u32x4 *>(sb + lds_off(wn * WN + fn * 32 + lr, ss * 2 + lh));
+        for (int ss = 0; ss < SUB; ++ss) {
+            const int cb = ss & 1, nb = cb ^ 1;
+            if (ss + 1 < SUB) {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    af[nb][fm] = *reinterpret_cast<const u32x4 *>(
+                        sa + lds_off<KB>(wm * WM + fm * 32 + lr, (ss + 1) * 2 + lh));
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    bfr[nb][fn] = *reinterpret_cast<const u32x4 *>(
+                        sb + lds_off<KB>(wn * WN + fn * 32 + lr, (ss + 1) * 2 + lh));
+            }
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
-                    mfma_chunk(TI{}, af[fm], bfr[fn], acc[fm][fn]);
+                    mfma_chunk(TI{}, af[cb][fm], bfr[cb][fn], acc[fm][fn]);
         }
+        __builtin_amdgcn_iglp_opt(1);
     }
 
-    // Full K loop with a double-buffered LDS tile; ends with a barrier so the
-    // caller may reuse `smem`.
-    __device__ __forceinline__ void run(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb,
-                                        int klen, int tid, f32x16 (&acc)[FM][FN])
+    // Wait for this wave's copies of stage kt when `ahead` later stages were
+    // queued after it (their copies may stay in flight).
+    __device__ __forceinline__ void wait_stage(int ahead)
     {
-        const int wave = tid >> 6, lane = tid & 63;
-        const int wm = wave / NWN, wn = wave % NWN;
+        constexpr int PER = A_LD + B_LD;
+        static_assert(PER * (STAGES - 2) <= 63, "vmcnt range");
+        if (ahead <= 0 || STAGES == 2)
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        else if (ahead == 1 || STAGES == 3)
+            __builtin_amdgcn_s_waitcnt(0x0070 | (PER & 15) | ((PER >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0070 | ((2 * PER) & 15) | (((2 * PER) >> 4) << 14));
+    }
+
+    // Full K loop: an STAGES-deep ring of LDS buffers fed by global->LDS
+    // copies issued STAGES-1 stages ahead; one barrier per stage.  Ends with a
+    // barrier so the caller may reuse `smem`.
+    __device__ __forceinline__ void run(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb, int klen,
+                                        int tid, f32x16 (&acc)[FM][FN])
+    {
+        const int lane = tid & 63;
+        const int wm = (tid >> 6) / NWN, wn = (tid >> 6) % NWN;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -274,21 +344,54 @@ struct GemmCore {
                     acc[fm][fn][i] = 0.f;
         setup(p, m0, n0, m_used, kb, tid);
         const int nk = klen / KT;
-        constexpr int BUF = LDS_A + LDS_B;
-        load(0);
-        store(smem, smem + LDS_A);
-        __syncthreads();
-        for (int kt = 0; kt + 1 < nk; ++kt) {
-            char *cur = smem + (kt & 1) * BUF;
-            char *nxt = smem + ((kt + 1) & 1) * BUF;
-            load(kt + 1);
-            compute(cur, cur + LDS_A, wm, wn, lane, acc);
-            store(nxt, nxt + LDS_A);
+        if constexpr (B_KN) {
+            load(0, smem);
+            store_b(smem);
+            wait_stage(0);
+            __syncthreads();
+            for (int kt = 0; kt + 1 < nk; ++kt) {
+                char *cur = smem + (kt & 1) * BUF;
+                char *nxt = smem + ((kt + 1) & 1) * BUF;
+                load(kt + 1, nxt);
+                compute(cur, wm, wn, lane, acc);
+                store_b(nxt);
+                wait_stage(0);
+                __syncthreads();
+            }
+            compute(smem + ((nk - 1) & 1) * BUF, wm, wn, lane, acc);
+            __syncthreads();
+        } else if constexpr (STAGES == 2) {
+            load(0, smem);
+            wait_stage(0);
+            __syncthreads();
+            for (int kt = 0; kt + 1 < nk; ++kt) {
+                load(kt + 1, smem + ((kt + 1) & 1) * BUF);
+                compute(smem + (kt & 1) * BUF, wm, wn, lane, acc);
+                wait_stage(0);
+                __syncthreads();
+            }
+            compute(smem + ((nk - 1) & 1) * BUF, wm, wn, lane, acc);
+            __syncthreads();
+        } else {
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s)
+                if (s < nk)
+                    load(s, smem + s * BUF);
+            int slot = 0;  // buffer of stage kt
+            for (int kt = 0; kt < nk; ++kt) {
+                const int left = nk - 1 - kt;  // stages queued after kt
+                wait_stage(left < STAGES - 2 ? left : STAGES - 2);
+                __syncthreads();
+                if (kt + STAGES - 1 < nk) {
+                    int ls = slot + STAGES - 1;
+                    ls = ls >= STAGES ? ls - STAGES : ls;
+                    load(kt + STAGES - 1, smem + ls * BUF);
+                }
+                compute(smem + slot * BUF, wm, wn, lane, acc);
+                slot = slot + 1 == STAGES ? 0 : slot + 1;
+            }
             __syncthreads();
         }
-        char *last = smem + ((nk - 1) & 1) * BUF;
-        compute(last, last + LDS_A, wm, wn, lane, acc);
-        __syncthreads();
     }
 };
 
