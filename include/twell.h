@@ -29,7 +29,7 @@
  *     are inactive).  Inside a tile, entries appear in ascending column order.
  *     cnt holds the TRUE number of actives of a (row, tile), which may exceed
  *     cap; only the cap lowest columns are stored.  Slots at or past
- *     min(cnt, cap) are left untouched (undefined content).
+ *     min(cnt, cap) hold value 0 and index 0.
  *   - Inputs must be finite, except that the bias column of W_g^T may hold
  *     -inf (a dead neuron: never active).
  *   - Errors the host can see return a negative status BEFORE anything is
@@ -101,8 +101,7 @@ typedef struct twell_hybrid_t {
  *   x    : device [h->T][d], vdtype h->vdtype
  *   wg_t : device [h->F][d], vdtype h->vdtype (column d-1 may hold -inf)
  *   d    : model width, multiple of 64
- *   h    : output TwELL; writes h->cnt fully and the kept slots of h->val,
- *          h->idx.
+ *   h    : output TwELL; writes every element of h->cnt, h->val, h->idx.
  * Returns TWELL_OK or a negative twell_status. */
 TWELL_API int twell_pack_gate(const void *x, const void *wg_t, int32_t d, const twell_t *h, void *stream);
 

@@ -40,6 +40,8 @@ def run_hip(wl, max_ovf=None, stream=None):
     hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
     # poison the outputs so stale memory cannot pass a check
     hy.ell.cnt.fill_(-7)
+    hy.ell.idx.fill_(0xAB)
+    hy.ell.val.fill_(-3.0)
     hy.row_ovf.fill_(-7)
     hy.n_ovf.fill_(-7)
     y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
@@ -79,9 +81,9 @@ def compare(wl, out, ref=None, rows=None, check_y=True, label=""):
     rows = ref.rows
     cnt = out["cnt"][rows]
     np.testing.assert_array_equal(cnt, ref.tw.cnt, err_msg=f"{label}: TwELL counts")
-    kept = ref.tw.kept()
-    np.testing.assert_array_equal(out["idx"][rows][kept], ref.tw.idx[kept], err_msg=f"{label}: TwELL indices")
-    np.testing.assert_array_equal(out["val"][rows][kept], ref.tw.val[kept].astype(np.float32),
+    # kept slots and the zero padding past min(cnt, cap), bit for bit
+    np.testing.assert_array_equal(out["idx"][rows], ref.tw.idx, err_msg=f"{label}: TwELL indices")
+    np.testing.assert_array_equal(out["val"][rows], ref.tw.val.astype(np.float32),
                                   err_msg=f"{label}: TwELL values")
     np.testing.assert_array_equal(out["row_ovf"][rows], ref.row_ovf, err_msg=f"{label}: row_ovf")
     # the overflow list is a property of all rows: it must be exactly the ascending list

@@ -30,9 +30,12 @@ int check_layout(const twell_t *h, int32_t d)
     // The fused step keeps a token's row in registers: at most 8 KiB per row.
     if ((int64_t)d * elem_size(h->vdtype) > 8192)
         return TWELL_E_UNSUPPORTED;
-    // GEMM operands are addressed with 32-bit byte offsets: each matrix < 4 GiB.
+    // GEMM operands are addressed with 32-bit byte offsets: each matrix < 4 GiB;
+    // TwELL slots with 32-bit element offsets: T * n_b * cap < 2^31.
     const int64_t lim = (int64_t)1 << 32;
     if ((int64_t)h->T * d * elem_size(h->vdtype) >= lim || (int64_t)h->F * d * elem_size(h->vdtype) >= lim)
+        return TWELL_E_SHAPE;
+    if ((int64_t)h->T * (h->F / w) * h->cap >= ((int64_t)1 << 31))
         return TWELL_E_SHAPE;
     return TWELL_OK;
 }

@@ -19,10 +19,16 @@
 #include "launch.h"
 #include "twell_device.h"
 
+#ifndef FUSED_G
+#define FUSED_G 2
+#endif
+
 namespace twell {
 
-constexpr int LIST_MAX = 512;  // entries staged per pass (8 bytes each)
-constexpr int NWV = 4;         // waves per token
+#ifndef FUSED_WAVES
+#define FUSED_WAVES 4
+#endif
+constexpr int NWV = FUSED_WAVES;  // waves per token
 
 template <typename TI> struct FusedArgs {
     const int32_t *cnt;
@@ -67,73 +73,113 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane)
     return v;
 }
 
-// G entries (j, h) of the list at `e0`: y += (h * (x . W_u^T[j])) * W_d[j].
-template <typename TI, int NC, int G>
-__device__ __forceinline__ void fused_group(const FusedArgs<TI> &a, const int2 *list, int e0, int lane,
-                                            int64_t row_bytes, const float (&xf)[NC][Elt<TI>::PER_CHUNK],
-                                            float (&yacc)[NC][Elt<TI>::PER_CHUNK])
-{
-    constexpr int E = Elt<TI>::PER_CHUNK;
-    int j[G];
-    float h[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int2 en = list[e0 + g];
-        j[g] = __builtin_amdgcn_readfirstlane(en.x);
-        h[g] = __int_as_float(__builtin_amdgcn_readfirstlane(en.y));
-    }
+// Weight rows of G list entries in registers.
+template <typename TI, int NC, int G> struct Group {
     u32x4 wu[G][NC], wv[G][NC];
+    float h[G];
+};
+
+// Request the W_u^T and W_d rows of entries e0 .. e0+G-1.
+template <typename TI, int NC, int G>
+__device__ __forceinline__ void group_load(const FusedArgs<TI> &a, const int2 *list, int e0, int lane,
+                                           int64_t row_bytes, Group<TI, NC, G> &g)
+{
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int k = 0; k < G; ++k) {
+        const int2 en = list[e0 + k];
+        const int j = __builtin_amdgcn_readfirstlane(en.x);
+        g.h[k] = __int_as_float(__builtin_amdgcn_readfirstlane(en.y));
+        const char *pu = (const char *)a.wu_t + (int64_t)j * row_bytes;
+        const char *pd = (const char *)a.wd + (int64_t)j * row_bytes;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int ch = lane + 64 * c;
             const bool ok = ch < a.nchunks;
-            wu[g][c] = ok ? ldg16((const char *)a.wu_t + (int64_t)j[g] * row_bytes + ch * 16) : u32x4{0, 0, 0, 0};
-            wv[g][c] = ok ? ldg16((const char *)a.wd + (int64_t)j[g] * row_bytes + ch * 16) : u32x4{0, 0, 0, 0};
+            g.wu[k][c] = ok ? ldg16(pu + ch * 16) : u32x4{0, 0, 0, 0};
+            g.wv[k][c] = ok ? ldg16(pd + ch * 16) : u32x4{0, 0, 0, 0};
         }
+    }
+}
+
+// y += (h * (x . W_u^T[j])) * W_d[j] for the entries of a loaded group.
+template <typename TI, int NC, int G>
+__device__ __forceinline__ void group_apply(const Group<TI, NC, G> &g, const float (&xf)[NC][Elt<TI>::PER_CHUNK],
+                                            float (&yacc)[NC][Elt<TI>::PER_CHUNK])
+{
+    constexpr int E = Elt<TI>::PER_CHUNK;
     float part[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int k = 0; k < G; ++k) {
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                s = fmaf(xf[c][e], chunk_elem<TI>(wu[g][c], e), s);
-        part[g] = s;
+                s = fmaf(xf[c][e], chunk_elem<TI>(g.wu[k][c], e), s);
+        part[k] = s;
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        part[g] = wave_sum(part[g]);
+    for (int k = 0; k < G; ++k)
+        part[k] = wave_sum(part[k]);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float sc = h[g] * part[g];
+    for (int k = 0; k < G; ++k) {
+        const float sc = g.h[k] * part[k];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                yacc[c][e] = fmaf(sc, chunk_elem<TI>(wv[g][c], e), yacc[c][e]);
+                yacc[c][e] = fmaf(sc, chunk_elem<TI>(g.wv[k][c], e), yacc[c][e]);
     }
 }
 
-// One workgroup of NWV waves per token.  Wave 0 stages the token's entries
-// (ascending j) into LDS; wave w then takes the groups of G entries numbered
-// w, w + NWV, w + 2 NWV, ...; the NWV partial y rows meet in LDS and are added
-// in wave order.  Tokens without entries, and overflow rows, get y = 0.
+// This wave's groups q = q0, q0 + step, ... < ngroups, in order, with the next
+// group's rows requested before the current group is reduced.
+template <typename TI, int NC, int G>
+__device__ __forceinline__ void group_stream(const FusedArgs<TI> &a, const int2 *list, int q0, int step, int ngroups,
+                                             int lane, int64_t row_bytes, const float (&xf)[NC][Elt<TI>::PER_CHUNK],
+                                             float (&yacc)[NC][Elt<TI>::PER_CHUNK])
+{
+    Group<TI, NC, G> ga, gb;
+    int q = q0;
+    if (q < ngroups)
+        group_load<TI, NC, G>(a, list, q * G, lane, row_bytes, ga);
+    while (q < ngroups) {
+        if (q + step < ngroups)
+            group_load<TI, NC, G>(a, list, (q + step) * G, lane, row_bytes, gb);
+        group_apply<TI, NC, G>(ga, xf, yacc);
+        q += step;
+        if (q >= ngroups)
+            break;
+        if (q + step < ngroups)
+            group_load<TI, NC, G>(a, list, (q + step) * G, lane, row_bytes, ga);
+        group_apply<TI, NC, G>(gb, xf, yacc);
+        q += step;
+    }
+}
+
+// One workgroup of NWV waves per token.  Wave w owns the TwELL tiles
+// b = w, w + NWV, w + 2 NWV, ...: it reads their counts, indices and values
+// itself, compacts its entries (ascending tile, then slot) into a private LDS
+// list of at most WLIST entries at a time, and streams them G at a time.  No
+// barrier is needed until the NWV partial y rows meet in LDS, where every wave
+// adds a quarter of the columns in wave order.  Tokens without entries and
+// overflow rows get y = 0.
+constexpr int WLIST = 128;  // entries per wave per pass
+
 template <typename TI, int NC, int G>
 __global__ __launch_bounds__(64 * NWV) void ffn_fused_kernel(FusedArgs<TI> a)
 {
     constexpr int E = Elt<TI>::PER_CHUNK;
     constexpr int YW = NC * 64 * E;  // floats of one partial y row (>= d)
-    __shared__ int2 list[LIST_MAX];
-    __shared__ __attribute__((aligned(16))) float part[NWV - 1][YW];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    __shared__ int2 wlist[NWV][WLIST];
+    __shared__ __attribute__((aligned(16))) float part[NWV][YW];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = blockIdx.x;
     const int64_t row_bytes = (int64_t)a.d * Elt<TI>::SIZE;
     float *yrow = a.y + (int64_t)t * a.d;
 
-    // Overflow test and number of kept entries (every wave, same values).
+    // Overflow test over the whole row (every wave, same answer).
     const int32_t *crow = a.cnt + (int64_t)t * a.n_b;
     bool ovf = false;
     int total = 0;
@@ -161,72 +207,85 @@ __global__ __launch_bounds__(64 * NWV) void ffn_fused_kernel(FusedArgs<TI> a)
             yacc[c][e] = 0.f;
         }
     }
-    for (int win = 0; win < total; win += LIST_MAX) {
-        if (wave == 0) {
-            // Stage entries [win, win + LIST_MAX) in ascending (tile, slot) order.
-            int base = 0;
-            for (int b0 = 0; b0 < a.n_b; b0 += 64) {
-                const int b = b0 + lane;
-                int c = b < a.n_b ? crow[b] : 0;
-                c = c < a.cap ? c : a.cap;
-                const int incl = wave_incl_scan(c, lane);
-                const int excl = base + incl - c;
-                const int64_t slot0 = ((int64_t)t * a.n_b + b) * a.cap;
+
+    // This wave's tiles: b = wave + NWV * l for l = 0, 1, ...; lane l holds tile l.
+    const int my_tiles = (a.n_b - wave + NWV - 1) / NWV;
+    const bool vec = a.cap % 16 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 15u) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.val) & 15u) == 0;
+    int2 *list = wlist[wave];
+    for (int l0 = 0; l0 < my_tiles; l0 += 64) {
+        const int l = l0 + lane;
+        const int b = wave + NWV * l;
+        int c = l < my_tiles ? crow[b] : 0;
+        c = c < a.cap ? c : a.cap;
+        const int incl = wave_incl_scan(c, lane);
+        const int ctot = __shfl(incl, 63, 64);
+        const int64_t slot0 = ((int64_t)t * a.n_b + b) * a.cap;
+        for (int win = 0; win < ctot; win += WLIST) {
+            const int excl = incl - c - win;  // position of this tile's first entry in the window
+            if (vec) {
+                for (int s0 = 0; s0 < c; s0 += 16) {
+                    if (excl + s0 >= WLIST || excl + s0 + 16 <= 0)
+                        continue;
+                    const u32x4 iw = ldg16(a.idx + slot0 + s0);
+                    u32x4 vw[16 / E];
+#pragma unroll
+                    for (int q = 0; q < 16 / E; ++q)
+                        vw[q] = ldg16(a.val + slot0 + s0 + q * E);
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) {
+                        const int pos = excl + s0 + k;
+                        if (s0 + k < c && pos >= 0 && pos < WLIST) {
+                            int j = b * a.tile_w + (int)((iw[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+                            j = j < a.F ? j : a.F - 1;  // memory safety for a corrupt index
+                            list[pos] = make_int2(j, __float_as_int(chunk_elem<TI>(vw[k / E], k % E)));
+                        }
+                    }
+                }
+            } else {
                 for (int s = 0; s < c; ++s) {
-                    const int pos = excl + s - win;
-                    if (pos >= 0 && pos < LIST_MAX) {
+                    const int pos = excl + s;
+                    if (pos >= 0 && pos < WLIST) {
                         int j = b * a.tile_w + a.idx[slot0 + s];
                         j = j < a.F ? j : a.F - 1;  // memory safety for a corrupt index
                         list[pos] = make_int2(j, __float_as_int(load_elem(a.val + slot0 + s)));
                     }
                 }
-                base += __shfl(incl, 63, 64);
             }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's list stores are done
+            __builtin_amdgcn_wave_barrier();
+            const int n = ctot - win < WLIST ? ctot - win : WLIST;
+            const int ngroups = n / G;
+            group_stream<TI, NC, G>(a, list, 0, 1, ngroups, lane, row_bytes, xf, yacc);
+            for (int e0 = ngroups * G; e0 < n; ++e0) {
+                Group<TI, NC, 1> g1;
+                group_load<TI, NC, 1>(a, list, e0, lane, row_bytes, g1);
+                group_apply<TI, NC, 1>(g1, xf, yacc);
+            }
+            __builtin_amdgcn_wave_barrier();  // list reads done before the next window's stores
         }
-        __syncthreads();
-        const int n = total - win < LIST_MAX ? total - win : LIST_MAX;
-        const int ngroups = n / G;
-        for (int q = wave; q < ngroups; q += NWV)
-            fused_group<TI, NC, G>(a, list, q * G, lane, row_bytes, xf, yacc);
-        // the tail entries (n % G), one at a time, on the wave whose turn is next
-        for (int e0 = ngroups * G; e0 < n; ++e0)
-            if (wave == (ngroups + (e0 - ngroups * G)) % NWV)
-                fused_group<TI, NC, 1>(a, list, e0, lane, row_bytes, xf, yacc);
-        __syncthreads();
     }
 
-    // Partial rows of waves 1.. meet wave 0's in LDS; y = ((p0 + p1) + p2) + p3.
-    if (wave > 0) {
+    // The NWV partial rows meet in LDS; wave w adds columns [w d/NWV, (w+1) d/NWV)
+    // as ((p0 + p1) + p2) + p3.
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int q = 0; q < E / 4; ++q)
-                *reinterpret_cast<float4 *>(&part[wave - 1][((lane + 64 * c) * E) + 4 * q]) =
-                    make_float4(yacc[c][4 * q], yacc[c][4 * q + 1], yacc[c][4 * q + 2], yacc[c][4 * q + 3]);
-    }
+        for (int q = 0; q < E / 4; ++q)
+            *reinterpret_cast<float4 *>(&part[wave][((lane + 64 * c) * E) + 4 * q]) =
+                make_float4(yacc[c][4 * q], yacc[c][4 * q + 1], yacc[c][4 * q + 2], yacc[c][4 * q + 3]);
     __syncthreads();
-    if (wave == 0) {
+    for (int i = tid * 4; i < a.d; i += 64 * NWV * 4) {
+        float4 acc4 = *reinterpret_cast<const float4 *>(&part[0][i]);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int ch = lane + 64 * c;
-            if (ch < a.nchunks) {
-                float4 *dst = reinterpret_cast<float4 *>(yrow + (int64_t)ch * E);
-#pragma unroll
-                for (int q = 0; q < E / 4; ++q) {
-                    float4 acc4 = make_float4(yacc[c][4 * q], yacc[c][4 * q + 1], yacc[c][4 * q + 2],
-                                              yacc[c][4 * q + 3]);
-#pragma unroll
-                    for (int w = 0; w < NWV - 1; ++w) {
-                        const float4 p4 = *reinterpret_cast<const float4 *>(&part[w][ch * E + 4 * q]);
-                        acc4.x += p4.x;
-                        acc4.y += p4.y;
-                        acc4.z += p4.z;
-                        acc4.w += p4.w;
-                    }
-                    dst[q] = acc4;
-                }
-            }
+        for (int w = 1; w < NWV; ++w) {
+            const float4 p4 = *reinterpret_cast<const float4 *>(&part[w][i]);
+            acc4.x += p4.x;
+            acc4.y += p4.y;
+            acc4.z += p4.z;
+            acc4.w += p4.w;
         }
+        *reinterpret_cast<float4 *>(yrow + i) = acc4;
     }
 }
 
@@ -235,7 +294,7 @@ static hipError_t fused_go(const FusedArgs<TI> &a, hipStream_t s)
 {
     if (a.T == 0)
         return hipSuccess;
-    ffn_fused_kernel<TI, NC, 4><<<dim3(a.T), dim3(64 * NWV), 0, s>>>(a);
+    ffn_fused_kernel<TI, NC, FUSED_G><<<dim3(a.T), dim3(64 * NWV), 0, s>>>(a);
     return hipGetLastError();
 }
 

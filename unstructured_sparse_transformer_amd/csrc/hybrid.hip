@@ -6,7 +6,7 @@
 // Steps on the device, all on the caller's stream with no host round trip:
 //   row_flags     row_ovf[t] = some tile of row t has cnt > cap
 //   compact_rows  one workgroup turns the flags into the ascending overflow-row
-//                 list and its length (ballot + popcount prefix, no atomics)
+//                 list and its length (workgroup prefix sum, no atomics)
 //   dense_gate    ReLU(x . W_g) for the listed rows  -> dense backup
 //   gated_up      round(dense * (x . W_u))  for the listed rows -> workspace
 //   down          (gated product) . W_d     -> y rows of the listed tokens
@@ -18,6 +18,8 @@
 namespace twell {
 
 // ------------------------------------------------------------------ partition
+// One thread per row; VEC: the row's counts are read as 16-byte vectors.
+template <bool VEC>
 __global__ __launch_bounds__(256) void row_flags_kernel(const int32_t *__restrict__ cnt, int T, int n_b, int cap,
                                                         int32_t *__restrict__ row_ovf)
 {
@@ -26,36 +28,65 @@ __global__ __launch_bounds__(256) void row_flags_kernel(const int32_t *__restric
         return;
     const int32_t *c = cnt + (int64_t)t * n_b;
     int f = 0;
-    for (int b = 0; b < n_b; ++b)
-        f |= c[b] > cap;
+    if constexpr (VEC) {
+        for (int b = 0; b < n_b; b += 4) {
+            const int4 v = *reinterpret_cast<const int4 *>(c + b);
+            f |= (v.x > cap) | (v.y > cap) | (v.z > cap) | (v.w > cap);
+        }
+    } else {
+        for (int b = 0; b < n_b; ++b)
+            f |= c[b] > cap;
+    }
     row_ovf[t] = f;
 }
 
-__global__ __launch_bounds__(1024) void compact_rows_kernel(const int32_t *__restrict__ row_ovf, int T, int max_ovf,
-                                                            int32_t *__restrict__ ovf_rows,
-                                                            int32_t *__restrict__ n_ovf)
+// One workgroup: thread i owns rows [base + 16 i, base + 16 i + 16) of each
+// 16384-row chunk; per-thread counts -> workgroup exclusive scan (ballot-free
+// wave scan + 16 wave totals in LDS) -> each thread writes its flagged rows in
+// ascending order.  n_ovf is the true number of flagged rows.
+constexpr int CR_THREADS = 1024, CR_ROWS = 16;
+
+__global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t *__restrict__ row_ovf, int T,
+                                                                  int max_ovf, int32_t *__restrict__ ovf_rows,
+                                                                  int32_t *__restrict__ n_ovf)
 {
-    __shared__ int wave_tot[16];
+    __shared__ int wave_tot[CR_THREADS / 64];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const uint64_t lower = lane ? (~0ull >> (64 - lane)) : 0ull;
     int base = 0;
-    for (int t0 = 0; t0 < T; t0 += 1024) {
-        const int t = t0 + tid;
-        const bool f = t < T && row_ovf[t] != 0;
-        const uint64_t m = __ballot(f);
-        if (lane == 0)
-            wave_tot[wave] = __popcll(m);
+    for (int t0 = 0; t0 < T; t0 += CR_THREADS * CR_ROWS) {
+        const int r0 = t0 + tid * CR_ROWS;
+        uint32_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < CR_ROWS; ++k) {
+            const int t = r0 + k;
+            bits |= (t < T && row_ovf[t] != 0) ? (1u << k) : 0u;
+        }
+        const int mine = __popc(bits);
+        int incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(incl, o, 64);
+            if (lane >= o)
+                incl += u;
+        }
+        if (lane == 63)
+            wave_tot[wave] = incl;
         __syncthreads();
         int off = 0, tot = 0;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) {
+        for (int w = 0; w < CR_THREADS / 64; ++w) {
             const int c = wave_tot[w];
             off += w < wave ? c : 0;
             tot += c;
         }
-        const int pos = base + off + __popcll(m & lower);
-        if (f && pos < max_ovf)
-            ovf_rows[pos] = t;
+        int pos = base + off + incl - mine;
+        while (bits) {
+            const int k = __ffs(bits) - 1;
+            bits &= bits - 1;
+            if (pos < max_ovf)
+                ovf_rows[pos] = r0 + k;
+            ++pos;
+        }
         base += tot;
         __syncthreads();
     }
@@ -65,14 +96,18 @@ __global__ __launch_bounds__(1024) void compact_rows_kernel(const int32_t *__res
 
 hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, hipStream_t s)
 {
-    row_flags_kernel<<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, T, n_b, cap, row_ovf);
+    const bool vec = (n_b % 4 == 0) && ((reinterpret_cast<uintptr_t>(cnt) & 15u) == 0);
+    if (vec)
+        row_flags_kernel<true><<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, T, n_b, cap, row_ovf);
+    else
+        row_flags_kernel<false><<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, T, n_b, cap, row_ovf);
     return hipGetLastError();
 }
 
 hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows, int32_t *n_ovf,
                                hipStream_t s)
 {
-    compact_rows_kernel<<<dim3(1), dim3(1024), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf);
+    compact_rows_kernel<<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf);
     return hipGetLastError();
 }
 
@@ -92,7 +127,7 @@ __device__ __forceinline__ int rows_used(const GemmArgs &p)
 template <typename TI, int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dense_epi_kernel(GemmArgs p, DenseOut<TI> o)
 {
-    using Core = GemmCore<TI, BM, BN, WM, WN, false>;
+    using Core = GemmCore<TI, BM, BN, WM, WN, false, 64, 4>;
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
     const int m_used = rows_used(p);
     int mt, nt;
@@ -188,8 +223,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
     }
 }
 
-// Small-M tile shape for the hybrid GEMMs: 64 x 128 per workgroup, 4 waves.
+// Small-M tile shapes for the hybrid GEMMs (M = overflow rows, a few hundred):
+// gate / up: 64 x 128 per workgroup, 4 waves, 4-deep global->LDS ring;
+// down: 64 x 256, 4 waves, split over K so enough workgroups stream W_d.
 constexpr int HB_BM = 64, HB_BN = 128, HB_WM = 32, HB_WN = 64;
+constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32, DN_WN = 128;
 
 template <typename TI, int MODE>
 static hipError_t dense_go(const void *x, int T, const void *w_t, const int32_t *ovf_rows, const int32_t *n_ovf,
@@ -237,11 +275,12 @@ hipError_t launch_gated_up(int vdtype, const void *x, int T, const void *wu_t, c
 
 int down_splits(int max_ovf, int F, int d)
 {
-    // Aim for >= ~512 workgroups when every listed row is used; K slices stay
-    // whole multiples of 64 elements.
-    const long tiles = (long)((max_ovf + HB_BM - 1) / HB_BM) * ((d + HB_BN - 1) / HB_BN);
+    // Overflow rows are typically a few percent of max_ovf's worth of M tiles;
+    // aim for >= ~2048 workgroups over the full M range so that the active
+    // ones cover the chip.  K slices stay whole multiples of 64 elements.
+    const long tiles = (long)((max_ovf + DN_BM - 1) / DN_BM) * ((d + DN_BN - 1) / DN_BN);
     int s = 1;
-    while (s < 8 && tiles * s < 512 && F % (s * 2 * 64) == 0)
+    while (s < 8 && tiles * s < 2048 && F % (s * 2 * 64) == 0)
         s *= 2;
     return s;
 }
@@ -263,13 +302,13 @@ static hipError_t down_go(const void *pbuf, const void *wd, const int32_t *ovf_r
     p.k_begin = 0;
     p.k_len = F;
     p.k_split_len = F / splits;
-    p.MT = (max_ovf + HB_BM - 1) / HB_BM;
-    p.NT = (d + HB_BN - 1) / HB_BN;
+    p.MT = (max_ovf + DN_BM - 1) / DN_BM;
+    p.NT = (d + DN_BN - 1) / DN_BN;
     p.a_bytes = (uint32_t)((int64_t)max_ovf * F * sizeof(TI));
     p.b_bytes = 0;  // KN-layout B is read through plain pointers
     DownOut<TI> o{part, y, ovf_rows, splits};
-    down_kernel<TI, HB_BM, HB_BN, HB_WM, HB_WN>
-        <<<dim3(p.MT * p.NT, splits), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);
+    down_kernel<TI, DN_BM, DN_BN, DN_WM, DN_WN>
+        <<<dim3(p.MT * p.NT, splits), dim3((DN_BM / DN_WM) * (DN_BN / DN_WN) * 64), 0, s>>>(p, o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;

@@ -17,6 +17,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef GEMM_IGLP
+#define GEMM_IGLP 0
+#endif
+
 namespace twell {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -183,7 +187,7 @@ struct GemmCore {
     // swizzle maps to that slot.
     __device__ __forceinline__ void setup(const GemmArgs &p, int m0, int n0, int m_used, int kb, int tid)
     {
-        wave = tid >> 6;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
         const int lane = tid & 63;
         constexpr int RPW_LOG = KB == 128 ? 1 : 2;
         ra = make_rsrc(p.A, p.a_bytes);
@@ -310,7 +314,9 @@ struct GemmCore {
                 for (int fn = 0; fn < FN; ++fn)
                     mfma_chunk(TI{}, af[cb][fm], bfr[cb][fn], acc[fm][fn]);
         }
-        __builtin_amdgcn_iglp_opt(1);
+        __builtin_amdgcn_iglp_opt(GEMM_IGLP);
+        // nothing of this stage may sink below the wait for the next stage's copies
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // Wait for this wave's copies of stage kt when `ahead` later stages were
@@ -334,7 +340,8 @@ struct GemmCore {
                                         int tid, f32x16 (&acc)[FM][FN])
     {
         const int lane = tid & 63;
-        const int wm = (tid >> 6) / NWN, wn = (tid >> 6) % NWN;
+        const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wv / NWN, wn = wv % NWN;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
