@@ -127,7 +127,7 @@ __device__ __forceinline__ int rows_used(const GemmArgs &p)
 template <typename TI, int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dense_epi_kernel(GemmArgs p, DenseOut<TI> o)
 {
-    using Core = GemmCore<TI, BM, BN, WM, WN, false, 64, 4>;
+    using Core = GemmCore<TI, BM, BN, WM, WN, false, 64, 8>;
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
     const int m_used = rows_used(p);
     int mt, nt;
@@ -169,7 +169,7 @@ template <typename TI> struct DownOut {
 template <typename TI, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void down_kernel(GemmArgs p, DownOut<TI> o)
 {
-    using Core = GemmCore<TI, BM, BN, WM, WN, true>;
+    using Core = GemmCore<TI, BM, BN, WM, WN, true, 64, 4>;
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
     const int m_used = rows_used(p);
     int mt, nt;
@@ -223,9 +223,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
     }
 }
 
-// Small-M tile shapes for the hybrid GEMMs (M = overflow rows, a few hundred):
-// gate / up: 64 x 128 per workgroup, 4 waves, 4-deep global->LDS ring;
-// down: 64 x 256, 4 waves, split over K so enough workgroups stream W_d.
+// Small-M tile shapes for the hybrid GEMMs (M = overflow rows, a few hundred;
+// they stream whole weight matrices, so each workgroup keeps many K stages of
+// copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 8-deep ring of
+// 64-byte K stages; down: 64 x 256, 4 waves, 4-deep ring with the W_d stage
+// transposed in LDS, split over K.
 constexpr int HB_BM = 64, HB_BN = 128, HB_WM = 32, HB_WN = 64;
 constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32, DN_WN = 128;
 
@@ -305,7 +307,7 @@ static hipError_t down_go(const void *pbuf, const void *wd, const int32_t *ovf_r
     p.MT = (max_ovf + DN_BM - 1) / DN_BM;
     p.NT = (d + DN_BN - 1) / DN_BN;
     p.a_bytes = (uint32_t)((int64_t)max_ovf * F * sizeof(TI));
-    p.b_bytes = 0;  // KN-layout B is read through plain pointers
+    p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
     DownOut<TI> o{part, y, ovf_rows, splits};
     down_kernel<TI, DN_BM, DN_BN, DN_WM, DN_WN>
         <<<dim3(p.MT * p.NT, splits), dim3((DN_BM / DN_WM) * (DN_BN / DN_WN) * 64), 0, s>>>(p, o);

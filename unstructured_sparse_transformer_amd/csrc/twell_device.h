@@ -152,45 +152,48 @@ struct GemmCore {
     static constexpr int FM = WM / 32, FN = WN / 32;
     static constexpr int E = Elt<TI>::PER_CHUNK;
     static constexpr int SZ = Elt<TI>::SIZE;
-    static constexpr int CPR = KB / 16;                  // chunks per tile row
+    static constexpr int CPR = KB / 16;                  // chunks per operand tile row
     static constexpr int KT = KB / SZ;                   // K elements per stage
     static constexpr int SUB = KB / 32;                  // MFMA sub-steps per stage
-    static constexpr int RPC = 1024 / KB;                // tile rows per 1 KiB copy
-    // K-contiguous operands arrive by global->LDS copies of 1 KiB per wave
-    // instruction (RPC whole tile rows).
-    static constexpr int A_LD = BM / RPC / NW;
-    static constexpr int B_LD = B_KN ? 0 : BN / RPC / NW;
-    static constexpr int B_UNITS = B_KN ? CPR * BN / E : 0;  // E x E transpose units per stage
-    static constexpr int B_UPT = B_KN ? (B_UNITS + NTHR - 1) / NTHR : 0;
+    static constexpr int RPC = 1024 / KB;                // operand tile rows per 1 KiB copy
     static constexpr int LDS_A = BM * KB, LDS_B = BN * KB;
-    static constexpr int BUF = LDS_A + LDS_B;
-    static constexpr int LDS_BYTES = STAGES * BUF;
+    // K-contiguous ("NK") operands arrive by global->LDS copies of 1 KiB per
+    // wave instruction (RPC whole operand rows).  A KN-layout B ([K][N],
+    // N-contiguous) arrives the same way as raw [KT][BN] rows and is transposed
+    // inside LDS, 8 x 8 (bf16) or 4 x 4 (fp32) blocks at a time, into the
+    // operand layout before the stage's MFMAs.
+    static constexpr int RAW_ROW = BN * SZ;              // bytes of one raw B row
+    static constexpr int B_RAW = B_KN ? KT * RAW_ROW : 0;
+    static constexpr int RAW_RPI = B_KN ? 1024 / RAW_ROW : 1;  // raw rows per 1 KiB copy
+    static constexpr int A_LD = BM / RPC / NW;
+    static constexpr int B_LD = B_KN ? KT / RAW_RPI / NW : BN / RPC / NW;
+    static constexpr int B_UNITS = B_KN ? (KT / E) * (BN / E) : 0;  // transpose blocks per stage
+    static constexpr int BUF = LDS_A + (B_KN ? B_RAW : LDS_B);       // one ring slot
+    static constexpr int LDS_BYTES = STAGES * BUF + (B_KN ? LDS_B : 0);
     static_assert(KB == 64 || KB == 128, "stage row width");
-    static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
-    static_assert(!B_KN || STAGES == 2, "the register-transposed B path is double-buffered only");
+    static_assert(STAGES >= 2 && STAGES <= 8, "pipeline depth");
     static_assert((BM / RPC) % NW == 0, "A tile rows split over the waves");
     static_assert(B_KN || (BN / RPC) % NW == 0, "B tile rows split over the waves");
+    static_assert(!B_KN || (1024 % RAW_ROW == 0 && (KT / RAW_RPI) % NW == 0), "raw B rows split over the waves");
+    static_assert(!B_KN || B_UNITS % NTHR == 0 || B_UNITS < NTHR, "transpose blocks split over the threads");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is whole 32x32 blocks");
 
     __amdgpu_buffer_rsrc_t ra, rb;
     int a_voff[A_LD];
     int b_voff[B_LD > 0 ? B_LD : 1];
-    u32x4 b_reg[B_KN ? (B_UPT * E) : 1];
-    const char *bkn_ptr[B_KN ? B_UPT : 1];
-    int bkn_row0[B_KN ? B_UPT : 1], bkn_chunk[B_KN ? B_UPT : 1];
-    bool bkn_on[B_KN ? B_UPT : 1];
-    int64_t ldb_bytes;
     int wave;
+    int b_stage_bytes;  // KN: bytes of K rows per stage in global memory
 
-    // Lane l of copy j of this wave fills tile row g*RPC + l/CPR (g = j*NW + wave)
-    // at physical chunk slot l%CPR, i.e. it loads the logical chunk that the
-    // swizzle maps to that slot.
+    // Copy j of this wave fills operand rows g*RPC + l/CPR (g = j*NW + wave) at
+    // physical chunk slot l%CPR, i.e. it loads the logical chunk the swizzle
+    // maps there.  KN raw copies fill raw rows g*RAW_RPI + l/(RAW_ROW/16).
     __device__ __forceinline__ void setup(const GemmArgs &p, int m0, int n0, int m_used, int kb, int tid)
     {
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
         const int lane = tid & 63;
         constexpr int RPW_LOG = KB == 128 ? 1 : 2;
         ra = make_rsrc(p.A, p.a_bytes);
+        rb = make_rsrc(p.B, p.b_bytes);
 #pragma unroll
         for (int j = 0; j < A_LD; ++j) {
             const int r = (j * NW + wave) * RPC + lane / CPR;
@@ -201,7 +204,6 @@ struct GemmCore {
             a_voff[j] = (int)((ar * p.lda + kb) * SZ + c * 16);
         }
         if constexpr (!B_KN) {
-            rb = make_rsrc(p.B, p.b_bytes);
 #pragma unroll
             for (int j = 0; j < B_LD; ++j) {
                 const int r = (j * NW + wave) * RPC + lane / CPR;
@@ -211,26 +213,23 @@ struct GemmCore {
                 b_voff[j] = (int)(((int64_t)gn * p.ldb + kb) * SZ + c * 16);
             }
         } else {
-            ldb_bytes = p.ldb * SZ;
+            constexpr int LPR = RAW_ROW / 16;  // lanes per raw row
+            b_stage_bytes = KT * (int)p.ldb * SZ;
 #pragma unroll
-            for (int i = 0; i < B_UPT; ++i) {
-                const int u = tid + i * NTHR;
-                bkn_on[i] = u < B_UNITS;
-                const int kg = u % CPR, ng = u / CPR;  // k group (chunk within the stage), n group
-                int gn = n0 + ng * E;
-                gn = gn <= p.N - E ? gn : p.N - E;
-                bkn_ptr[i] = (const char *)p.B + ((int64_t)(kb + kg * E) * p.ldb + gn) * SZ;
-                bkn_row0[i] = ng * E;
-                bkn_chunk[i] = kg;
+            for (int j = 0; j < B_LD; ++j) {
+                const int r = (j * NW + wave) * RAW_RPI + lane / LPR;  // k row within the stage
+                int gn = n0 + (lane % LPR) * E;
+                gn = gn <= p.N - E ? gn : p.N - E;  // columns past N re-read valid ones; results discarded
+                b_voff[j] = (int)(((int64_t)(kb + r) * p.ldb + gn) * SZ);
             }
         }
     }
 
-    // Queue stage kt's global->LDS copies into buffer `buf`; KN-layout B goes to registers.
+    // Queue stage kt's global->LDS copies into ring slot `buf`.
     __device__ __forceinline__ void load(int kt, char *buf)
     {
-        const int koff = kt * KB;
         char *sa = buf, *sb = buf + LDS_A;
+        const int koff = kt * KB;
 #pragma unroll
         for (int j = 0; j < A_LD; ++j)
             dma16(ra, sa + (j * NW + wave) * 1024, a_voff[j], koff);
@@ -239,54 +238,57 @@ struct GemmCore {
             for (int j = 0; j < B_LD; ++j)
                 dma16(rb, sb + (j * NW + wave) * 1024, b_voff[j], koff);
         } else {
-            const int64_t krow = (int64_t)kt * KT * ldb_bytes;
+            const int boff = (int)((uint32_t)kt * (uint32_t)b_stage_bytes);
 #pragma unroll
-            for (int i = 0; i < B_UPT; ++i)
-                if (bkn_on[i]) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        b_reg[i * E + e] = ldg16(bkn_ptr[i] + krow + e * ldb_bytes);
-                }
+            for (int j = 0; j < B_LD; ++j)
+                dma16(rb, sb + (j * NW + wave) * 1024, b_voff[j], boff);
         }
     }
 
-    // KN-layout B: registers -> LDS, transposed so each column's K run is one chunk.
-    __device__ __forceinline__ void store_b(char *buf)
+    // KN: raw [KT][BN] rows of slot `buf` -> operand layout in `bop`.
+    // Thread u handles the E x E block at k-group u / (BN/E), n-group u % (BN/E).
+    __device__ __forceinline__ void transpose_b(const char *buf, char *bop, int tid)
     {
         if constexpr (B_KN) {
-            char *sb = buf + LDS_A;
+            const char *raw = buf + LDS_A;
 #pragma unroll
-            for (int i = 0; i < B_UPT; ++i)
-                if (bkn_on[i]) {
-                    // b_reg[i*E + e] holds row k = e, columns n = 0..E-1
+            for (int u0 = 0; u0 < B_UNITS; u0 += NTHR) {
+                const int u = u0 + tid;
+                if (B_UNITS < NTHR && u >= B_UNITS)
+                    break;
+                const int ng = u % (BN / E), kg = u / (BN / E);
+                u32x4 rr[E];
 #pragma unroll
-                    for (int n = 0; n < E; ++n) {
-                        u32x4 o;
-                        if constexpr (SZ == 2) {
+                for (int e = 0; e < E; ++e)
+                    rr[e] = *reinterpret_cast<const u32x4 *>(raw + (kg * E + e) * RAW_ROW + ng * 16);
 #pragma unroll
-                            for (int w = 0; w < 4; ++w) {
-                                const uint32_t lo = b_reg[i * E + 2 * w][n >> 1];
-                                const uint32_t hi = b_reg[i * E + 2 * w + 1][n >> 1];
-                                const uint32_t l16 = (n & 1) ? (lo >> 16) : (lo & 0xFFFFu);
-                                const uint32_t h16 = (n & 1) ? (hi >> 16) : (hi & 0xFFFFu);
-                                o[w] = l16 | (h16 << 16);
-                            }
-                        } else {
+                for (int n = 0; n < E; ++n) {
+                    u32x4 o;
+                    if constexpr (SZ == 2) {
 #pragma unroll
-                            for (int w = 0; w < 4; ++w)
-                                o[w] = b_reg[i * E + w][n];
+                        for (int w = 0; w < 4; ++w) {
+                            const uint32_t lo = rr[2 * w][n >> 1];
+                            const uint32_t hi = rr[2 * w + 1][n >> 1];
+                            const uint32_t l16 = (n & 1) ? (lo >> 16) : (lo & 0xFFFFu);
+                            const uint32_t h16 = (n & 1) ? (hi >> 16) : (hi & 0xFFFFu);
+                            o[w] = l16 | (h16 << 16);
                         }
-                        *reinterpret_cast<u32x4 *>(sb + lds_off<KB>(bkn_row0[i] + n, bkn_chunk[i])) = o;
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            o[w] = rr[w][n];
                     }
+                    *reinterpret_cast<u32x4 *>(bop + lds_off<KB>(ng * E + n, kg)) = o;
                 }
+            }
         }
     }
 
     // The MFMA sub-steps of one stage; fragments of sub-step s+1 are read from
     // LDS while the MFMAs of sub-step s run.
-    __device__ __forceinline__ void compute(const char *buf, int wm, int wn, int lane, f32x16 (&acc)[FM][FN])
+    __device__ __forceinline__ void compute(const char *sa, const char *sb, int wm, int wn, int lane,
+                                            f32x16 (&acc)[FM][FN])
     {
-        const char *sa = buf, *sb = buf + LDS_A;
         const int lr = lane & 31, lh = lane >> 5;
         u32x4 af[2][FM], bfr[2][FN];
 #pragma unroll
@@ -320,22 +322,31 @@ struct GemmCore {
     }
 
     // Wait for this wave's copies of stage kt when `ahead` later stages were
-    // queued after it (their copies may stay in flight).
-    __device__ __forceinline__ void wait_stage(int ahead)
+    // queued after it (their copies may stay in flight).  Also drains LDS ops.
+    template <int AHEAD> __device__ __forceinline__ static void wait_n()
     {
         constexpr int PER = A_LD + B_LD;
-        static_assert(PER * (STAGES - 2) <= 63, "vmcnt range");
-        if (ahead <= 0 || STAGES == 2)
-            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-        else if (ahead == 1 || STAGES == 3)
-            __builtin_amdgcn_s_waitcnt(0x0070 | (PER & 15) | ((PER >> 4) << 14));
-        else
-            __builtin_amdgcn_s_waitcnt(0x0070 | ((2 * PER) & 15) | (((2 * PER) >> 4) << 14));
+        constexpr int V = AHEAD * PER;
+        static_assert(V <= 63, "vmcnt range");
+        __builtin_amdgcn_s_waitcnt(0x0070 | (V & 15) | ((V >> 4) << 14));
     }
+    template <int N> __device__ __forceinline__ static void wait_upto(int ahead)
+    {
+        if constexpr (N == 0) {
+            wait_n<0>();
+        } else {
+            if (ahead >= N)
+                wait_n<N>();
+            else
+                wait_upto<N - 1>(ahead);
+        }
+    }
+    __device__ __forceinline__ void wait_stage(int ahead) { wait_upto<STAGES - 2>(ahead); }
 
-    // Full K loop: an STAGES-deep ring of LDS buffers fed by global->LDS
-    // copies issued STAGES-1 stages ahead; one barrier per stage.  Ends with a
-    // barrier so the caller may reuse `smem`.
+    // Full K loop: an STAGES-deep ring of LDS slots fed by global->LDS copies
+    // issued STAGES-1 stages ahead; one barrier per stage (two for a KN B, whose
+    // stage is transposed in LDS first).  Ends with a barrier so the caller may
+    // reuse `smem`.
     __device__ __forceinline__ void run(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb, int klen,
                                         int tid, f32x16 (&acc)[FM][FN])
     {
@@ -351,54 +362,31 @@ struct GemmCore {
                     acc[fm][fn][i] = 0.f;
         setup(p, m0, n0, m_used, kb, tid);
         const int nk = klen / KT;
-        if constexpr (B_KN) {
-            load(0, smem);
-            store_b(smem);
-            wait_stage(0);
-            __syncthreads();
-            for (int kt = 0; kt + 1 < nk; ++kt) {
-                char *cur = smem + (kt & 1) * BUF;
-                char *nxt = smem + ((kt + 1) & 1) * BUF;
-                load(kt + 1, nxt);
-                compute(cur, wm, wn, lane, acc);
-                store_b(nxt);
-                wait_stage(0);
-                __syncthreads();
-            }
-            compute(smem + ((nk - 1) & 1) * BUF, wm, wn, lane, acc);
-            __syncthreads();
-        } else if constexpr (STAGES == 2) {
-            load(0, smem);
-            wait_stage(0);
-            __syncthreads();
-            for (int kt = 0; kt + 1 < nk; ++kt) {
-                load(kt + 1, smem + ((kt + 1) & 1) * BUF);
-                compute(smem + (kt & 1) * BUF, wm, wn, lane, acc);
-                wait_stage(0);
-                __syncthreads();
-            }
-            compute(smem + ((nk - 1) & 1) * BUF, wm, wn, lane, acc);
-            __syncthreads();
-        } else {
+        char *bop = smem + STAGES * BUF;  // KN operand tile
 #pragma unroll
-            for (int s = 0; s < STAGES - 1; ++s)
-                if (s < nk)
-                    load(s, smem + s * BUF);
-            int slot = 0;  // buffer of stage kt
-            for (int kt = 0; kt < nk; ++kt) {
-                const int left = nk - 1 - kt;  // stages queued after kt
-                wait_stage(left < STAGES - 2 ? left : STAGES - 2);
-                __syncthreads();
-                if (kt + STAGES - 1 < nk) {
-                    int ls = slot + STAGES - 1;
-                    ls = ls >= STAGES ? ls - STAGES : ls;
-                    load(kt + STAGES - 1, smem + ls * BUF);
-                }
-                compute(smem + slot * BUF, wm, wn, lane, acc);
-                slot = slot + 1 == STAGES ? 0 : slot + 1;
-            }
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nk)
+                load(s, smem + s * BUF);
+        int slot = 0;  // ring slot of stage kt
+        for (int kt = 0; kt < nk; ++kt) {
+            const int left = nk - 1 - kt;  // stages queued after kt
+            wait_stage(left < STAGES - 2 ? left : STAGES - 2);
             __syncthreads();
+            char *cur = smem + slot * BUF;
+            if constexpr (B_KN) {
+                transpose_b(cur, bop, tid);
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                __syncthreads();
+            }
+            if (kt + STAGES - 1 < nk) {
+                int ls = slot + STAGES - 1;
+                ls = ls >= STAGES ? ls - STAGES : ls;
+                load(kt + STAGES - 1, smem + ls * BUF);
+            }
+            compute(cur, B_KN ? bop : cur + LDS_A, wm, wn, lane, acc);
+            slot = slot + 1 == STAGES ? 0 : slot + 1;
         }
+        __syncthreads();
     }
 };
 
