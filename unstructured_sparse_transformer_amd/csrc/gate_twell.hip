@@ -16,21 +16,25 @@
 #include "launch.h"
 #include "twell_device.h"
 
-// bf16 workgroup tile: GATE_BM x 256 with 4 waves of (GATE_BM/2) x 128;
-// GATE_WPE waves per SIMD (1: one 256-row workgroup per CU, 256 accumulator
-// registers per wave; 2: two 128-row workgroups per CU, so one's epilogue
-// overlaps the other's MFMAs).
+// bf16 workgroup tile: GATE_BM x 256 with waves of GATE_WM x 128 and
+// GATE_WPE waves per SIMD.  Default: 256 x 256 with 8 waves of 64 x 128 (two
+// per SIMD, so one wave's LDS reads and barrier waits overlap the other's
+// MFMAs) fed by a 3-deep ring of 64-byte K stages (96 KiB of LDS).  A 256-wide
+// tile moves 2/3 of the L2->LDS bytes per flop of a 128 x 256 one.
 #ifndef GATE_BM
-#define GATE_BM 128
+#define GATE_BM 256
 #endif
 #ifndef GATE_WPE
 #define GATE_WPE 2
+#endif
+#ifndef GATE_WM
+#define GATE_WM 64
 #endif
 #ifndef GATE_KB
 #define GATE_KB 64
 #endif
 #ifndef GATE_STAGES
-#define GATE_STAGES 2
+#define GATE_STAGES 3
 #endif
 
 namespace twell {
@@ -283,13 +287,12 @@ static hipError_t gate_twell_go(const void *x, const void *wg_t, int T, int d, i
     return hipGetLastError();
 }
 
-// Tile shapes: bf16 256 x 256 per workgroup (4 waves of 128 x 128, 256
-// accumulator registers each), fp32 64 x 256.
+// Tile shapes: bf16 as configured above, fp32 64 x 256 (4 waves of 32 x 128).
 hipError_t launch_gate_twell(int vdtype, const void *x, const void *wg_t, int T, int d, int F, int tile_w, int cap,
                              void *val, uint8_t *idx, int32_t *cnt, hipStream_t s)
 {
     if (vdtype == 1)
-        return gate_twell_go<__bf16, GATE_BM, 256, GATE_BM / 2, 128, GATE_KB, GATE_STAGES, GATE_WPE>(x, wg_t, T, d, F,
+        return gate_twell_go<__bf16, GATE_BM, 256, GATE_WM, 128, GATE_KB, GATE_STAGES, GATE_WPE>(x, wg_t, T, d, F,
                                                                                                tile_w, cap, val,
                                                                               idx, cnt, s);
     return gate_twell_go<float, 64, 256, 32, 128, 128, 2, 1>(x, wg_t, T, d, F, tile_w, cap, val, idx, cnt, s);

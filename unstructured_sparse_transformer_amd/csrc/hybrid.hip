@@ -111,6 +111,25 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
     return hipGetLastError();
 }
 
+#ifndef HB_BN
+#define HB_BN 128
+#endif
+#ifndef HB_WN
+#define HB_WN 64
+#endif
+#ifndef HB_KB
+#define HB_KB 128
+#endif
+#ifndef HB_STAGES
+#define HB_STAGES 4
+#endif
+#ifndef DN_KB
+#define DN_KB 128
+#endif
+#ifndef DN_STAGES
+#define DN_STAGES 3
+#endif
+
 // ------------------------------------------------------------------ dense GEMMs
 template <typename TI> struct DenseOut {
     TI *out;            // [max_ovf][N]
@@ -127,7 +146,7 @@ __device__ __forceinline__ int rows_used(const GemmArgs &p)
 template <typename TI, int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dense_epi_kernel(GemmArgs p, DenseOut<TI> o)
 {
-    using Core = GemmCore<TI, BM, BN, WM, WN, false, 64, 8>;
+    using Core = GemmCore<TI, BM, BN, WM, WN, false, HB_KB, HB_STAGES>;
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
     const int m_used = rows_used(p);
     int mt, nt;
@@ -169,7 +188,7 @@ template <typename TI> struct DownOut {
 template <typename TI, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void down_kernel(GemmArgs p, DownOut<TI> o)
 {
-    using Core = GemmCore<TI, BM, BN, WM, WN, true, 64, 4>;
+    using Core = GemmCore<TI, BM, BN, WM, WN, true, DN_KB, DN_STAGES>;
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
     const int m_used = rows_used(p);
     int mt, nt;
@@ -224,11 +243,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 }
 
 // Small-M tile shapes for the hybrid GEMMs (M = overflow rows, a few hundred;
-// they stream whole weight matrices, so each workgroup keeps many K stages of
-// copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 8-deep ring of
-// 64-byte K stages; down: 64 x 256, 4 waves, 4-deep ring with the W_d stage
-// transposed in LDS, split over K.
-constexpr int HB_BM = 64, HB_BN = 128, HB_WM = 32, HB_WN = 64;
+// they stream whole weight matrices, so each workgroup keeps several K stages
+// of copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 4-deep
+// ring of 128-byte K stages; down: 64 x 256, 4 waves, 3-deep ring with the
+// W_d stage transposed in LDS, split over K.
+constexpr int HB_BM = 64, HB_WM = 32;
 constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32, DN_WN = 128;
 
 template <typename TI, int MODE>

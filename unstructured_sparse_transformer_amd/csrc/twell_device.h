@@ -110,7 +110,7 @@ __device__ __forceinline__ void tile_coords(int g, int MT, int NT, int &mt, int 
 // C[m][n] = sum_k A[m][k] * B(k, n) over k in [k_begin, k_begin + k_len).
 // A rows are K-contiguous (optionally gathered through a_rows).  B is either
 // "NK" (B^T stored [N][K], K-contiguous: W_g^T, W_u^T) or "KN" ([K][N],
-// N-contiguous: W_d), the latter transposed in registers on its way to LDS.
+// N-contiguous: W_d), the latter transposed inside LDS stage by stage.
 struct GemmArgs {
     const void *A;
     int64_t lda;             // elements
@@ -138,6 +138,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *dst, int voff, int soff)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
+
+// Workgroup barrier without the release/acquire fence of __syncthreads(): that
+// fence makes the compiler wait for every outstanding global->LDS copy
+// (vmcnt(0)) before the barrier, which would drain a multi-stage copy ring at
+// each stage.  Callers wait for exactly what must be complete with their own
+// s_waitcnt first; the empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void wg_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Wait until this wave's outstanding vector-memory operations (including the
@@ -371,12 +384,12 @@ struct GemmCore {
         for (int kt = 0; kt < nk; ++kt) {
             const int left = nk - 1 - kt;  // stages queued after kt
             wait_stage(left < STAGES - 2 ? left : STAGES - 2);
-            __syncthreads();
+            wg_barrier();
             char *cur = smem + slot * BUF;
             if constexpr (B_KN) {
                 transpose_b(cur, bop, tid);
                 __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                __syncthreads();
+                wg_barrier();
             }
             if (kt + STAGES - 1 < nk) {
                 int ls = slot + STAGES - 1;
