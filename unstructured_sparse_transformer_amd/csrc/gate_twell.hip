@@ -19,8 +19,8 @@
 // bf16 workgroup tile: GATE_BM x 256 with waves of GATE_WM x 128 and
 // GATE_WPE waves per SIMD.  Default: 256 x 256 with 8 waves of 64 x 128 (two
 // per SIMD, so one wave's LDS reads and barrier waits overlap the other's
-// MFMAs) fed by a 3-deep ring of 64-byte K stages (96 KiB of LDS).  A 256-wide
-// tile moves 2/3 of the L2->LDS bytes per flop of a 128 x 256 one.
+// MFMAs) fed by a 2-deep ring of 128-byte K stages (128 KiB of LDS).  A
+// 256-wide tile moves 2/3 of the L2->LDS bytes per flop of a 128 x 256 one.
 #ifndef GATE_BM
 #define GATE_BM 256
 #endif
@@ -31,10 +31,10 @@
 #define GATE_WM 64
 #endif
 #ifndef GATE_KB
-#define GATE_KB 64
+#define GATE_KB 128
 #endif
 #ifndef GATE_STAGES
-#define GATE_STAGES 3
+#define GATE_STAGES 2
 #endif
 
 namespace twell {
@@ -46,22 +46,43 @@ template <typename TI> struct TwellOut {
     int cap, n_b;
 };
 
+// One staged TwELL slot: the stored value's bits with the tile-local column
+// above them (bf16: one 32-bit word; fp32: one 64-bit word).
+template <typename TI> struct StageWord;
+template <> struct StageWord<__bf16> {
+    using W = uint32_t;
+    __device__ static W pack(float v, int c)
+    {
+        const __bf16 h = (__bf16)v;
+        return (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)c << 16);
+    }
+    __device__ static uint32_t bits(W w) { return w & 0xFFFFu; }
+    __device__ static uint32_t col(W w) { return w >> 16; }
+};
+template <> struct StageWord<float> {
+    using W = uint64_t;
+    __device__ static W pack(float v, int c) { return (uint64_t)__float_as_uint(v) | ((uint64_t)c << 32); }
+    __device__ static uint32_t bits(W w) { return (uint32_t)w; }
+    __device__ static uint32_t col(W w) { return (uint32_t)(w >> 32); }
+};
+
 // Pack the accumulators of one BM x BN output tile into TwELL (tile width TW).
-// The unrolled part touches each accumulator register twice with a couple of
-// instructions; everything that depends on the (few) active values runs in
-// short loops, so the epilogue's code stays small next to the 64 KiB
-// instruction cache a CU pair shares.
+// Every active value goes to its slot straight from the MFMA accumulators,
+// in parallel: the slot of the value at (row, column c) is the number of
+// active columns of the row that precede c inside c's TwELL tile.
 //   pass 1 (per wave): one ballot per accumulator register gives two rows'
 //           32-bit activity masks for one 32-column block (the active test is
 //           the fp32 accumulator > 0); the 16 registers' masks are gathered
 //           into lanes 0-15 and stored as mask[row][block].
-//   pass 2 (one thread per row): popcount of each tile's masks -> the true
-//           count (stored, and kept in LDS).
-//   pass 3, per 32-row block fm of every wave: the block's values, rounded to
-//           the storage type, go to an LDS tile; then one thread per (row,
-//           tile) walks the set mask bits in ascending column order and puts
-//           the first `cap` (value, tile-local column) pairs in an LDS staging
-//           row (or straight to memory when staging does not fit).
+//   pass 2 (one thread per row): per tile, the popcount of its blocks' masks
+//           is the true count (stored, and kept in LDS); per block, the
+//           exclusive prefix of the popcounts inside its tile (a byte).
+//   pass 3 (per wave, per accumulator register): from its row's block mask
+//           each lane gets its rank among the active columns below it; slot =
+//           block prefix + rank.  Active values with slot < cap are written,
+//           rounded to the storage type and packed with their tile-local
+//           column, to an LDS staging row (or straight to memory when staging
+//           does not fit).
 //   pass 4 (one thread per (row, tile)): staged slots go out with 16-byte
 //           stores, slots past min(count, cap) as zeros.
 template <typename TI, int BM, int BN, int WM, int WN, int TW, int LDS_BYTES>
@@ -74,23 +95,22 @@ __device__ __forceinline__ void twell_epilogue(f32x16 (&acc)[WM / 32][WN / 32], 
     constexpr int TPW = BN / TW;  // TwELL tiles per workgroup row
     constexpr int NTHR = NWM * NWN * 64;
     constexpr int SZ = sizeof(TI);
-    constexpr int CROWS = NWM * 32;  // rows of one pass-3 block (block fm of every wave row)
+    using SW = StageWord<TI>;
+    using W = typename SW::W;
     static_assert(BN / 32 == 8, "a row's masks are 8 words");
+    static_assert(BPW == 4, "a wave's blocks are one mask vector and one prefix word");
     static_assert(BN % TW == 0, "the workgroup's columns cover whole TwELL tiles");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / NWN, wn = wave % NWN;
     const int cap = o.cap;
-    uint32_t *smask = reinterpret_cast<uint32_t *>(smem);        // [BM][8] block masks
-    int16_t *scnt = reinterpret_cast<int16_t *>(smem + BM * 32);  // [BM][TPW] true counts
-    constexpr int SV_OFF = BM * 32 + ((BM * TPW * 2 + 15) & ~15);
-    TI *sv = reinterpret_cast<TI *>(smem + SV_OFF);               // [CROWS][BN] values of one block
-    constexpr int STAGE_OFF = SV_OFF + CROWS * BN * SZ;
-    char *stage = smem + STAGE_OFF;  // [BM][TPW][cap] values, then [BM][TPW][cap] indices
-    const bool staged = STAGE_OFF + BM * TPW * cap * (SZ + 1) <= LDS_BYTES;
+    uint32_t *smask = reinterpret_cast<uint32_t *>(smem);            // [BM][8] block masks
+    uint32_t *spre = reinterpret_cast<uint32_t *>(smem + BM * 32);   // [BM][2] prefix bytes
+    int16_t *scnt = reinterpret_cast<int16_t *>(smem + BM * 40);     // [BM][TPW] true counts
+    constexpr int STAGE_OFF = BM * 40 + ((BM * TPW * 2 + 15) & ~15);
+    W *sw = reinterpret_cast<W *>(smem + STAGE_OFF);                 // [BM][TPW][cap] staged slots
+    const bool staged = STAGE_OFF + BM * TPW * cap * (int)sizeof(W) <= LDS_BYTES;
     static_assert(STAGE_OFF <= LDS_BYTES, "epilogue LDS");
-    TI *sval = reinterpret_cast<TI *>(stage);
-    uint8_t *sidx = reinterpret_cast<uint8_t *>(stage + BM * TPW * cap * SZ);
 
     // pass 1
 #pragma unroll
@@ -115,66 +135,67 @@ __device__ __forceinline__ void twell_epilogue(f32x16 (&acc)[WM / 32][WN / 32], 
 
     // pass 2
     for (int r = tid; r < BM; r += NTHR) {
+        const u32x4 mlo = *reinterpret_cast<const u32x4 *>(smask + r * 8);
+        const u32x4 mhi = *reinterpret_cast<const u32x4 *>(smask + r * 8 + 4);
+        uint32_t pre[2] = {0u, 0u};
+        int run = 0;
         const int t = m0 + r;
 #pragma unroll
-        for (int tl = 0; tl < TPW; ++tl) {
-            int n = 0;
-#pragma unroll
-            for (int b = 0; b < BPT; ++b)
-                n += __popc(smask[r * 8 + tl * BPT + b]);
-            scnt[r * TPW + tl] = (int16_t)n;
-            const int gcol = n0 + tl * TW;
-            if (t < M && gcol < N)
-                o.cnt[(int64_t)t * o.n_b + gcol / TW] = n;
-        }
-    }
-
-    // pass 3
-    const int lc = lane & 31;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-        __syncthreads();  // sv is free (previous block consumed; pass 2 done)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int col = wn * WN + fn * 32 + lc;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)  // every value: only active positions are read back
-                store_elem(sv + (wm * 32 + acc_row(i, lane)) * BN + col, acc[fm][fn][i]);
-        }
-        __syncthreads();
-        for (int e = tid; e < CROWS * TPW; e += NTHR) {
-            const int cr = e / TPW, tl = e - cr * TPW;  // row cr of the block: wave row cr / 32
-            const int r = (cr >> 5) * WM + fm * 32 + (cr & 31);
-            const int t = m0 + r;
-            const int gbase = n0 + tl * TW;
-            if (t >= M || gbase >= N)
-                continue;
-            const int off = (t * o.n_b + gbase / TW) * cap;
-            const int so = (r * TPW + tl) * cap;
-            int k = 0;
-            for (int b = 0; b < BPT && k < cap; ++b) {
-                uint32_t m = smask[r * 8 + tl * BPT + b];
-                while (m != 0u && k < cap) {
-                    const int c = b * 32 + __ffs(m) - 1;  // tile-local column, ascending
-                    m &= m - 1u;
-                    const TI v = sv[cr * BN + tl * TW + c];
-                    if (staged) {
-                        sval[so + k] = v;
-                        sidx[so + k] = (uint8_t)c;
-                    } else {
-                        o.val[off + k] = v;
-                        o.idx[off + k] = (uint8_t)c;
-                    }
-                    ++k;
-                }
+        for (int b = 0; b < 8; ++b) {
+            if (b % BPT == 0)
+                run = 0;
+            pre[b >> 2] |= (uint32_t)run << (8 * (b & 3));
+            run += __popc(b < 4 ? mlo[b] : mhi[b - 4]);
+            if (b % BPT == BPT - 1) {
+                const int tl = b / BPT;
+                scnt[r * TPW + tl] = (int16_t)run;
+                const int gcol = n0 + tl * TW;
+                if (t < M && gcol < N)
+                    o.cnt[(int64_t)t * o.n_b + gcol / TW] = run;
             }
         }
+        spre[r * 2] = pre[0];
+        spre[r * 2 + 1] = pre[1];
     }
     __syncthreads();
 
+    // pass 3
+    const int lc = lane & 31;
+    const uint32_t below = (1u << lc) - 1u;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = wm * WM + fm * 32 + acc_row(i, lane);
+            // this half-wave's row: the wave's four block masks and their prefixes
+            const u32x4 mw = *reinterpret_cast<const u32x4 *>(smask + r * 8 + wn * 4);
+            const uint32_t pw = spre[r * 2 + wn];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const uint32_t m = mw[fn];
+                const int slot = (int)((pw >> (8 * fn)) & 0xFFu) + __popc(m & below);
+                if (((m >> lc) & 1u) && slot < cap) {
+                    const float v = acc[fm][fn][i];
+                    const int blk = wn * BPW + fn, tl = blk / BPT;
+                    const int c = (blk % BPT) * 32 + lc;
+                    if (staged) {
+                        sw[(r * TPW + tl) * cap + slot] = SW::pack(v, c);
+                    } else {
+                        const int t = m0 + r, gcol = n0 + tl * TW;
+                        if (t < M && gcol < N) {
+                            const int64_t off = ((int64_t)t * o.n_b + gcol / TW) * cap + slot;
+                            store_elem(o.val + off, v);
+                            o.idx[off] = (uint8_t)c;
+                        }
+                    }
+                }
+            }
+        }
+    __syncthreads();
+
     // pass 4
-    const bool vval = staged && (cap * SZ) % 16 == 0 && (reinterpret_cast<uintptr_t>(o.val) & 15u) == 0;
-    const bool vidx = staged && cap % 8 == 0 && (reinterpret_cast<uintptr_t>(o.idx) & 7u) == 0;
+    const bool vec = staged && (cap * SZ) % 16 == 0 && cap % 16 == 0 &&
+                     (reinterpret_cast<uintptr_t>(o.val) & 15u) == 0 && (reinterpret_cast<uintptr_t>(o.idx) & 15u) == 0;
     for (int e = tid; e < BM * TPW; e += NTHR) {
         const int r = e / TPW, tl = e - r * TPW;
         const int t = m0 + r;
@@ -182,52 +203,54 @@ __device__ __forceinline__ void twell_epilogue(f32x16 (&acc)[WM / 32][WN / 32], 
         if (t >= M || gcol >= N)
             continue;
         const int kept = min((int)scnt[e], cap);
-        const int off = (t * o.n_b + gcol / TW) * cap;
-        if (vval) {
-            const TI *svr = sval + e * cap;
-            for (int s0 = 0; s0 < cap; s0 += 16 / SZ) {
-                u32x4 w = *reinterpret_cast<const u32x4 *>(svr + s0);
+        const int64_t off = ((int64_t)t * o.n_b + gcol / TW) * cap;
+        const W *sr = sw + e * cap;
+        if (vec) {
+            // 16 slots at a time: 16 indices (one 16-byte store) and 16 values
+            for (int s0 = 0; s0 < cap; s0 += 16) {
+                u32x4 iw = {0u, 0u, 0u, 0u};
+                uint32_t vb[16];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {  // zero the slots at or past `kept`
-                    if constexpr (SZ == 2) {
-                        const int sa = s0 + 2 * q;
-                        w[q] &= (sa < kept ? 0xFFFFu : 0u) | (sa + 1 < kept ? 0xFFFF0000u : 0u);
-                    } else {
-                        w[q] = s0 + q < kept ? w[q] : 0u;
+                for (int q = 0; q < 16; ++q) {
+                    const bool k = s0 + q < kept;
+                    const W w = k ? sr[s0 + q] : (W)0;
+                    vb[q] = SW::bits(w);
+                    iw[q >> 2] |= (k ? SW::col(w) : 0u) << (8 * (q & 3));
+                }
+                *reinterpret_cast<u32x4 *>(o.idx + off + s0) = iw;
+                if constexpr (SZ == 2) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        u32x4 v;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            v[q] = vb[h * 8 + 2 * q] | (vb[h * 8 + 2 * q + 1] << 16);
+                        *reinterpret_cast<u32x4 *>(o.val + off + s0 + h * 8) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        u32x4 v;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            v[q] = vb[h * 4 + q];
+                        *reinterpret_cast<u32x4 *>(o.val + off + s0 + h * 4) = v;
                     }
                 }
-                *reinterpret_cast<u32x4 *>(o.val + off + s0) = w;
             }
         } else {
             for (int s = 0; s < cap; ++s) {
                 if (s < kept) {
-                    if (staged)
-                        o.val[off + s] = sval[e * cap + s];
+                    if (staged) {
+                        const W w = sr[s];
+                        if constexpr (SZ == 2)
+                            reinterpret_cast<uint16_t *>(o.val)[off + s] = (uint16_t)SW::bits(w);
+                        else
+                            reinterpret_cast<uint32_t *>(o.val)[off + s] = SW::bits(w);
+                        o.idx[off + s] = (uint8_t)SW::col(w);
+                    }
                 } else {
                     store_elem(o.val + off + s, 0.f);
-                }
-            }
-        }
-        if (vidx) {
-            const uint8_t *si = sidx + e * cap;
-            for (int s0 = 0; s0 < cap; s0 += 8) {
-                uint2 w = *reinterpret_cast<const uint2 *>(si + s0);
-                uint32_t k0 = 0, k1 = 0;
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    k0 |= (s0 + bb < kept ? 0xFFu : 0u) << (8 * bb);
-                    k1 |= (s0 + 4 + bb < kept ? 0xFFu : 0u) << (8 * bb);
-                }
-                w.x &= k0;
-                w.y &= k1;
-                *reinterpret_cast<uint2 *>(o.idx + off + s0) = w;
-            }
-        } else {
-            for (int s = 0; s < cap; ++s) {
-                if (s < kept) {
-                    if (staged)
-                        o.idx[off + s] = sidx[e * cap + s];
-                } else {
                     o.idx[off + s] = 0;
                 }
             }

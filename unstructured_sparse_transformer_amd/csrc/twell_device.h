@@ -20,6 +20,9 @@
 #ifndef GEMM_IGLP
 #define GEMM_IGLP 0
 #endif
+#ifndef GEMM_PIPE
+#define GEMM_PIPE 1
+#endif
 
 namespace twell {
 
@@ -356,6 +359,94 @@ struct GemmCore {
     }
     __device__ __forceinline__ void wait_stage(int ahead) { wait_upto<STAGES - 2>(ahead); }
 
+    // Fragments of MFMA sub-step ss (16 bf16 / 4 fp32 K elements) from a slot.
+    __device__ __forceinline__ void read_frags(const char *sa, const char *sb, int wm, int wn, int lane, int ss,
+                                               u32x4 (&af)[FM], u32x4 (&bf)[FN])
+    {
+        const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            af[fm] = *reinterpret_cast<const u32x4 *>(sa + lds_off<KB>(wm * WM + fm * 32 + lr, ss * 2 + lh));
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            bf[fn] = *reinterpret_cast<const u32x4 *>(sb + lds_off<KB>(wn * WN + fn * 32 + lr, ss * 2 + lh));
+    }
+    __device__ __forceinline__ static void mfma_sub(const u32x4 (&af)[FM], const u32x4 (&bf)[FN],
+                                                    f32x16 (&acc)[FM][FN])
+    {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                mfma_chunk(TI{}, af[fm], bf[fn], acc[fm][fn]);
+    }
+
+    // K loop for NK operands, pipelined across stages: the wait and barrier
+    // for stage kt+1 come before the MFMAs of stage kt's last sub-step, so the
+    // first fragment reads of kt+1 overlap those MFMAs instead of following a
+    // barrier with the MFMA pipe idle.  Past that barrier every wave holds the
+    // rest of stage kt in registers, so the copy for stage kt+STAGES goes into
+    // stage kt's slot.  Ends with a barrier so the caller may reuse `smem`.
+    __device__ __forceinline__ void run_nk(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb,
+                                           int klen, int tid, f32x16 (&acc)[FM][FN])
+    {
+        static_assert(!B_KN && SUB % 2 == 0, "fragment buffers alternate within a stage");
+        const int lane = tid & 63;
+        const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wv / NWN, wn = wv % NWN;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[fm][fn][i] = 0.f;
+        setup(p, m0, n0, m_used, kb, tid);
+        const int nk = klen / KT;
+        if (nk > 0) {
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s)
+                if (s < nk)
+                    load(s, smem + s * BUF);
+            wait_stage(nk - 1 < STAGES - 2 ? nk - 1 : STAGES - 2);
+            wg_barrier();
+            u32x4 af[2][FM], bf[2][FN];
+            read_frags(smem, smem + LDS_A, wm, wn, lane, 0, af[0], bf[0]);
+            if (STAGES - 1 < nk)
+                load(STAGES - 1, smem + (STAGES - 1) * BUF);
+            int slot = 0;  // ring slot of stage kt (= kt % STAGES)
+            for (int kt = 0; kt < nk; ++kt) {
+                char *cur = smem + slot * BUF;
+                const int nslot = slot + 1 == STAGES ? 0 : slot + 1;
+#pragma unroll
+                for (int ss = 0; ss < SUB; ++ss) {
+                    const int cb = ss & 1, nb = cb ^ 1;
+                    if (ss + 1 < SUB) {
+                        read_frags(cur, cur + LDS_A, wm, wn, lane, ss + 1, af[nb], bf[nb]);
+                    } else {
+                        // earlier sub-steps' MFMAs stay above the waits
+                        __builtin_amdgcn_sched_barrier(0);
+                        // this stage's last fragments have arrived (on every path, so the
+                        // compiler adds no partial waits before the MFMAs below)
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    }
+                    if (ss + 1 == SUB && kt + 1 < nk) {
+                        const int left = nk - 2 - kt;  // stages queued after kt+1
+                        wait_stage(left < STAGES - 2 ? left : STAGES - 2);
+                        wg_barrier();
+                        const char *nxt = smem + nslot * BUF;
+                        read_frags(nxt, nxt + LDS_A, wm, wn, lane, 0, af[nb], bf[nb]);
+                        if (kt + STAGES < nk)
+                            load(kt + STAGES, cur);
+                    }
+                    mfma_sub(af[cb], bf[cb], acc);
+                }
+                slot = nslot;
+            }
+        }
+        __syncthreads();
+    }
+
     // Full K loop: an STAGES-deep ring of LDS slots fed by global->LDS copies
     // issued STAGES-1 stages ahead; one barrier per stage (two for a KN B, whose
     // stage is transposed in LDS first).  Ends with a barrier so the caller may
@@ -363,6 +454,10 @@ struct GemmCore {
     __device__ __forceinline__ void run(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb, int klen,
                                         int tid, f32x16 (&acc)[FM][FN])
     {
+        if constexpr (!B_KN && GEMM_PIPE) {
+            run_nk(p, smem, m0, n0, m_used, kb, klen, tid, acc);
+            return;
+        }
         const int lane = tid & 63;
         const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm = wv / NWN, wn = wv % NWN;
