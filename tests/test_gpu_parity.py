@@ -87,6 +87,8 @@ EDGE = [
     (70, 2048, 512, 128, 8, "f32", 0.1, 0.5, 0),       # fp32, largest fp32 row
     (90, 192, 640, 64, 8, "f32", 0.2, 0.3, 5),         # fp32 odd shapes
     (512, 256, 1024, 128, 3, "bf16", 0.4, 0.2, 0),     # nearly every row overflows
+    (200, 256, 1024, 256, 64, "bf16", 0.3, 0.5, 0),    # large cap (staging beyond LDS: general epilogue)
+    (96, 128, 512, 64, 48, "f32", 0.4, 0.5, 0),        # fp32, large cap, w = 64
 ]
 
 

@@ -258,6 +258,185 @@ __device__ __forceinline__ void twell_epilogue(f32x16 (&acc)[WM / 32][WN / 32], 
     }
 }
 
+// Segment form of the epilogue, used when the staging below fits in LDS.
+// A segment is the part of one row's TwELL tile that one wave holds (the whole
+// tile when the tile is no wider than a wave's columns, else a wave's share);
+// a single pass over the accumulators fills every segment, so the ballots are
+// taken once and only the (few) active values cost more than a compare.
+//   pass A (per wave, per accumulator register): the ballot gives two rows'
+//           32-bit activity masks for one 32-column block; a running count
+//           over the wave's blocks gives each active lane its rank inside its
+//           segment; active values with rank < cap are packed with their
+//           tile-local column into the segment's staging slots; the
+//           segments' true counts go to LDS.  All-zero ballots (most of them)
+//           skip the rest.
+//   pass B (one thread per (row, tile)): the tile's segments are joined in
+//           column order (the true count is their sum), and the first `cap`
+//           slots go out with 16-byte stores, slots past min(count, cap) as
+//           zeros.
+template <typename TI, int BN, int WN, int TW> struct SegShape {
+    static constexpr int SEGW = TW < WN ? TW : WN;  // columns of a segment
+    static constexpr int NSEG = BN / SEGW;          // segments per row
+    static constexpr int SPT = TW / SEGW;           // segments per tile
+    static constexpr int BPS = SEGW / 32;           // 32-column blocks per segment
+};
+template <typename TI, int BM, int BN, int WN, int TW, int LDS_BYTES>
+__host__ __device__ constexpr int seg_stage_off()
+{
+    return (BM * SegShape<TI, BN, WN, TW>::NSEG * 2 + 15) & ~15;
+}
+template <typename TI, int BM, int BN, int WN, int TW, int LDS_BYTES>
+__device__ __forceinline__ bool seg_fits(int cap)
+{
+    return seg_stage_off<TI, BM, BN, WN, TW, LDS_BYTES>() +
+               BM * SegShape<TI, BN, WN, TW>::NSEG * cap * (int)sizeof(typename StageWord<TI>::W) <=
+           LDS_BYTES;
+}
+
+template <typename TI, int BM, int BN, int WM, int WN, int TW, int LDS_BYTES>
+__device__ __forceinline__ void twell_epilogue_seg(f32x16 (&acc)[WM / 32][WN / 32], char *smem, int m0, int n0, int M,
+                                                   int N, const TwellOut<TI> &o)
+{
+    constexpr int FM = WM / 32, FN = WN / 32, NWN = BN / WN, NWM = BM / WM;
+    constexpr int NTHR = NWM * NWN * 64;
+    constexpr int SZ = sizeof(TI);
+    constexpr int TPW = BN / TW;
+    using SS = SegShape<TI, BN, WN, TW>;
+    constexpr int NSEG = SS::NSEG, SPT = SS::SPT, BPS = SS::BPS, SEGW = SS::SEGW;
+    static_assert(SPT <= 2, "a tile spans at most two waves");
+    using SW = StageWord<TI>;
+    using W = typename SW::W;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int cap = o.cap;
+    int16_t *scnt = reinterpret_cast<int16_t *>(smem);  // [BM][NSEG] segment true counts
+    W *sw = reinterpret_cast<W *>(smem + seg_stage_off<TI, BM, BN, WN, TW, LDS_BYTES>());  // [BM][NSEG][cap]
+
+    // pass A
+    const int lc = lane & 31;
+    const uint32_t below = (1u << lc) - 1u;
+    const bool lo_half = lane < 32;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        int cnt_lo[FN / BPS], cnt_hi[FN / BPS];  // lanes i (0..15) collect register i's row counts
+#pragma unroll
+        for (int q = 0; q < FN / BPS; ++q)
+            cnt_lo[q] = cnt_hi[q] = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = wm * WM + fm * 32 + acc_row(i, lane);
+            uint32_t pre_lo = 0, pre_hi = 0;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                if (fn % BPS == 0)
+                    pre_lo = pre_hi = 0;
+                const float v = acc[fm][fn][i];
+                const bool act = v > 0.f;
+                const uint64_t b = __ballot(act);
+                const uint32_t blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
+                if (b != 0u) {
+                    const uint32_t half = lo_half ? blo : bhi;
+                    const int slot = (int)(lo_half ? pre_lo : pre_hi) + __popc(half & below);
+                    if (act && slot < cap) {
+                        const int col = wn * WN + fn * 32;  // first column of the block in the workgroup
+                        const int seg = col / SEGW;
+                        sw[(r * NSEG + seg) * cap + slot] = SW::pack(v, col % TW + lc);
+                    }
+                    pre_lo += __popc(blo);
+                    pre_hi += __popc(bhi);
+                }
+                if (fn % BPS == BPS - 1) {
+                    cnt_lo[fn / BPS] = lane == i ? (int)pre_lo : cnt_lo[fn / BPS];
+                    cnt_hi[fn / BPS] = lane == i ? (int)pre_hi : cnt_hi[fn / BPS];
+                }
+            }
+        }
+        if (lane < 16) {
+            const int r = wm * WM + fm * 32 + acc_row(lane, 0);
+#pragma unroll
+            for (int q = 0; q < FN / BPS; ++q) {
+                const int seg = (wn * WN) / SEGW + q;
+                scnt[r * NSEG + seg] = (int16_t)cnt_lo[q];
+                scnt[(r + 4) * NSEG + seg] = (int16_t)cnt_hi[q];
+            }
+        }
+    }
+    __syncthreads();
+
+    // pass B
+    const bool vec = (cap * SZ) % 16 == 0 && cap % 16 == 0 && (reinterpret_cast<uintptr_t>(o.val) & 15u) == 0 &&
+                     (reinterpret_cast<uintptr_t>(o.idx) & 15u) == 0;
+    for (int e = tid; e < BM * TPW; e += NTHR) {
+        const int r = e / TPW, tl = e - r * TPW;
+        const int t = m0 + r;
+        const int gcol = n0 + tl * TW;
+        if (t >= M || gcol >= N)
+            continue;
+        const int s0 = r * NSEG + tl * SPT;  // first segment of the tile
+        const int c0 = scnt[s0];
+        const int c1 = SPT == 2 ? (int)scnt[s0 + 1] : 0;
+        const int total = c0 + c1;
+        const int64_t ooff = (int64_t)t * o.n_b + gcol / TW;
+        o.cnt[ooff] = total;
+        const int k0 = min(c0, cap);           // slots taken from the first segment
+        const int kept = min(total, cap);
+        const W *sr0 = sw + (int64_t)s0 * cap;
+        const W *sr1 = sr0 + cap;              // second segment (SPT == 2)
+        const int64_t off = ooff * cap;
+        if (vec) {
+            for (int b0 = 0; b0 < cap; b0 += 16) {
+                u32x4 iw = {0u, 0u, 0u, 0u};
+                uint32_t vb[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int sl = b0 + q;
+                    W w = (W)0;
+                    if (sl < k0)
+                        w = sr0[sl];
+                    else if (SPT == 2 && sl < kept)
+                        w = sr1[sl - k0];
+                    vb[q] = SW::bits(w);
+                    iw[q >> 2] |= (sl < kept ? SW::col(w) : 0u) << (8 * (q & 3));
+                }
+                *reinterpret_cast<u32x4 *>(o.idx + off + b0) = iw;
+                if constexpr (SZ == 2) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        u32x4 v;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            v[q] = vb[h * 8 + 2 * q] | (vb[h * 8 + 2 * q + 1] << 16);
+                        *reinterpret_cast<u32x4 *>(o.val + off + b0 + h * 8) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        u32x4 v;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            v[q] = vb[h * 4 + q];
+                        *reinterpret_cast<u32x4 *>(o.val + off + b0 + h * 4) = v;
+                    }
+                }
+            }
+        } else {
+            for (int sl = 0; sl < cap; ++sl) {
+                W w = (W)0;
+                if (sl < k0)
+                    w = sr0[sl];
+                else if (SPT == 2 && sl < kept)
+                    w = sr1[sl - k0];
+                if constexpr (SZ == 2)
+                    reinterpret_cast<uint16_t *>(o.val)[off + sl] = (uint16_t)SW::bits(w);
+                else
+                    reinterpret_cast<uint32_t *>(o.val)[off + sl] = SW::bits(w);
+                o.idx[off + sl] = (uint8_t)(sl < kept ? SW::col(w) : 0u);
+            }
+        }
+    }
+}
+
 template <typename TI, int BM, int BN, int WM, int WN, int TW, int KB, int STAGES, int WPE>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
 gate_twell_kernel(GemmArgs p, TwellOut<TI> o)
@@ -270,7 +449,10 @@ gate_twell_kernel(GemmArgs p, TwellOut<TI> o)
     Core core;
     f32x16 acc[Core::FM][Core::FN];
     core.run(p, smem, m0, n0, p.M, p.k_begin, p.k_len, threadIdx.x, acc);
-    twell_epilogue<TI, BM, BN, WM, WN, TW, Core::LDS_BYTES>(acc, smem, m0, n0, p.M, p.N, o);
+    if (seg_fits<TI, BM, BN, WN, TW, Core::LDS_BYTES>(o.cap))
+        twell_epilogue_seg<TI, BM, BN, WM, WN, TW, Core::LDS_BYTES>(acc, smem, m0, n0, p.M, p.N, o);
+    else
+        twell_epilogue<TI, BM, BN, WM, WN, TW, Core::LDS_BYTES>(acc, smem, m0, n0, p.M, p.N, o);
 }
 
 template <typename TI, int BM, int BN, int WM, int WN, int KB, int STAGES, int WPE>
