@@ -129,7 +129,7 @@ def main():
         tw.twell_partition_overflow(x, wg, hy)
         if ev:
             ev[2].record()
-        tw.twell_ffn_fused(hy.ell, x, wu, wd, y)
+        tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=hy.order)
         if ev:
             ev[3].record()
         tw.twell_ffn_overflow(hy, x, wu, wd, y, ws)

@@ -93,6 +93,8 @@ typedef struct twell_hybrid_t {
     int32_t *ovf_rows; /* device [max_ovf]: overflow rows, ascending */
     int32_t *n_ovf;    /* device [1]: number of overflow rows (may exceed max_ovf) */
     void *dense;       /* device [max_ovf][F] vdtype: h_g rows of the overflow tokens */
+    int32_t *order;    /* device [T]: a permutation of the rows, the fused step's work
+                          order (rows with more stored entries first) */
 } twell_hybrid_t;
 
 /* Gate GEMM with the TwELL epilogue (section 2.1 of the page: x . W_g, ReLU
@@ -110,7 +112,12 @@ TWELL_API int twell_pack_gate(const void *x, const void *wg_t, int32_t d, const 
  * ovf_rows list and n_ovf, then recomputes ReLU(x . W_g) for the first
  * min(n_ovf, max_ovf) overflow rows into hy->dense.  Rows past max_ovf are
  * counted in n_ovf but get no dense row: the caller checks n_ovf <= max_ovf
- * after synchronising and retries with larger buffers otherwise. */
+ * after synchronising and retries with larger buffers otherwise.
+ * Also writes hy->order: the rows grouped by their number of stored entries
+ * e = sum over tiles of min(cnt, cap) (e = 0 for overflow rows) into the
+ * classes e >= 256, 192..255, 128..191, 64..127, 32..63, 16..31, 1..15, 0,
+ * heaviest class first and ascending rows inside a class (per chunk of
+ * 16384 rows).  It is a schedule only: no result depends on it. */
 TWELL_API int twell_partition_overflow(const void *x, const void *wg_t, int32_t d,
                              const twell_hybrid_t *hy, void *stream);
 
@@ -123,9 +130,14 @@ TWELL_API int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d,
  * (fp32), y[t] += (val * u) * W_d[j] (fp32).  Only the kept rows of W_u^T
  * and W_d are read.  Rows with some cnt > cap (overflow rows) get y = 0;
  * rows without actives get y = 0.
- *   x, wu_t, wd : device, vdtype h->vdtype;  y : device [h->T][d] float. */
-TWELL_API int twell_ffn_fused(const twell_t *h, const void *x, const void *wu_t, const void *wd,
-                    int32_t d, float *y, void *stream);
+ *   x, wu_t, wd : device, vdtype h->vdtype;  y : device [h->T][d] float.
+ *   order : optional device [h->T] permutation of 0..T-1 (as written by
+ *           twell_partition_overflow): rows are started in that order, so the
+ *           heavy ones do not trail at the end; NULL = ascending rows.  Each
+ *           row's result is the same bits for any order; a non-permutation
+ *           leaves some rows unwritten (entries are range-checked). */
+TWELL_API int twell_ffn_fused(const twell_t *h, const int32_t *order, const void *x, const void *wu_t,
+                    const void *wd, int32_t d, float *y, void *stream);
 
 /* Bytes of device workspace twell_ffn_hybrid needs for these sizes. */
 TWELL_API size_t twell_ffn_hybrid_workspace_bytes(int32_t max_ovf, int32_t F, int32_t d, int32_t vdtype);
@@ -140,9 +152,9 @@ TWELL_API size_t twell_ffn_hybrid_workspace_bytes(int32_t max_ovf, int32_t F, in
 TWELL_API int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
                        int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Hybrid FFN: twell_ffn_fused for all rows (overflow rows get 0), then
- * twell_ffn_overflow for the overflow rows; every row of y is the full FFN
- * output when n_ovf <= max_ovf. */
+/* Hybrid FFN: twell_ffn_fused for all rows in hy->order (overflow rows get
+ * 0), then twell_ffn_overflow for the overflow rows; every row of y is the
+ * full FFN output when n_ovf <= max_ovf. */
 TWELL_API int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
                      int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
 

@@ -44,12 +44,15 @@ def run_hip(wl, max_ovf=None, stream=None):
     hy.ell.val.fill_(-3.0)
     hy.row_ovf.fill_(-7)
     hy.n_ovf.fill_(-7)
+    hy.order.fill_(-7)
     y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
     yf = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    yo = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
     ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt)
     tw.twell_pack_gate_hybrid(x, wg, hy, stream)
     tw.twell_ffn_hybrid(hy, x, wu, wd, y, ws, stream)
-    tw.twell_ffn_fused(hy.ell, x, wu, wd, yf, stream)
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, yf, stream)                 # ascending rows
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, yo, stream, order=hy.order)  # work order
     torch.cuda.synchronize()
     n_ovf = int(hy.n_ovf.item())
     m = min(n_ovf, max_ovf)
@@ -63,8 +66,31 @@ def run_hip(wl, max_ovf=None, stream=None):
         "dense": hy.dense[:m].float().cpu().numpy(),
         "y": y.cpu().numpy(),
         "y_fused": yf.cpu().numpy(),
+        "y_fused_order": yo.cpu().numpy(),
+        "order": hy.order.cpu().numpy(),
         "max_ovf": max_ovf,
     }
+
+
+# Work classes of the fused step's schedule (the C header's definition):
+# stored entries e >= 256, 192..255, 128..191, 64..127, 32..63, 16..31, 1..15, 0.
+WORK_EDGES = (1, 16, 32, 64, 128, 192, 256)
+ORDER_CHUNK = 16384
+
+
+def check_order(wl, out, label=""):
+    """hy.order: a permutation of the rows; per chunk of 16384 rows, work
+    classes from the heaviest, ascending rows inside a class."""
+    cnt = out["cnt"]
+    ovf = (cnt > wl.cap).any(1)
+    e = np.where(ovf, 0, np.minimum(cnt, wl.cap).sum(1))
+    cls = np.searchsorted(np.array(WORK_EDGES), e, side="right")
+    order = out["order"]
+    assert np.array_equal(np.sort(order), np.arange(wl.T)), f"{label}: order is not a permutation"
+    for c0 in range(0, wl.T, ORDER_CHUNK):
+        rows = np.arange(c0, min(wl.T, c0 + ORDER_CHUNK))
+        want = rows[np.lexsort((rows, -cls[rows]))]
+        np.testing.assert_array_equal(order[rows], want, err_msg=f"{label}: work order")
 
 
 def row_rel_err(a, b):
@@ -86,6 +112,7 @@ def compare(wl, out, ref=None, rows=None, check_y=True, label=""):
     np.testing.assert_array_equal(out["val"][rows], ref.tw.val.astype(np.float32),
                                   err_msg=f"{label}: TwELL values")
     np.testing.assert_array_equal(out["row_ovf"][rows], ref.row_ovf, err_msg=f"{label}: row_ovf")
+    check_order(wl, out, label)
     # the overflow list is a property of all rows: it must be exactly the ascending list
     # of rows whose GPU counts exceed cap (checked against the oracle's flags on `rows`)
     all_ovf = np.nonzero((out["cnt"] > wl.cap).any(1))[0]
@@ -112,6 +139,9 @@ def compare(wl, out, ref=None, rows=None, check_y=True, label=""):
     bad = covered & ~zero & (num > Y_RTOL * den)
     assert not bad.any(), f"{label}: y rows off by more than {Y_RTOL}: {np.nonzero(bad)[0][:10]} " \
                           f"max rel {np.max(num[~zero] / den[~zero]):.3g}"
+    # the work order changes no bits
+    np.testing.assert_array_equal(out["y_fused_order"][rows], out["y_fused"][rows],
+                                  err_msg=f"{label}: fused result depends on the work order")
     # fused-only: overflow rows are 0, TwELL rows equal the hybrid's TwELL rows bit for bit
     ok = ref.row_ovf == 0
     assert not yf[~ok].any(), f"{label}: fused-only output must zero overflow rows"

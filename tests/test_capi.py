@@ -66,19 +66,24 @@ def test_pack_gate_validation():
 def test_fused_and_hybrid_validation():
     lib = tw.load()
     d = _desc()
-    assert lib.twell_ffn_fused(ctypes.byref(d), GOOD, GOOD, GOOD, 64, None, None) == -1   # y NULL
-    assert lib.twell_ffn_fused(ctypes.byref(d), GOOD, GOOD, GOOD + 4, 64, GOOD, None) == -2
-    assert lib.twell_ffn_fused(ctypes.byref(d), GOOD, GOOD, GOOD, 60, GOOD, None) == -3
-    hy = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD)
+    assert lib.twell_ffn_fused(ctypes.byref(d), None, GOOD, GOOD, GOOD, 64, None, None) == -1   # y NULL
+    assert lib.twell_ffn_fused(ctypes.byref(d), None, GOOD, GOOD, GOOD + 4, 64, GOOD, None) == -2
+    assert lib.twell_ffn_fused(ctypes.byref(d), None, GOOD, GOOD, GOOD, 60, GOOD, None) == -3
+    assert lib.twell_ffn_fused(ctypes.byref(d), GOOD + 2, GOOD, GOOD, GOOD, 64, GOOD, None) == -2  # order
+    hy = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
     need = lib.twell_ffn_hybrid_workspace_bytes(8, 512, 64, 1)
     assert need > 0
     assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, None, 0, None) == -6
     assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, GOOD, need - 1, None) == -6
     assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, GOOD + 16, need, None) == -2
-    bad = tw.TwellHybridT(d, -1, 0, GOOD, GOOD, GOOD, GOOD)
+    bad = tw.TwellHybridT(d, -1, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, ctypes.byref(bad), None) == -3
-    nod = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, None)
+    nod = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, None, GOOD)
     assert lib.twell_pack_gate_hybrid(GOOD, GOOD, 64, ctypes.byref(nod), None) == -1
+    noo = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD, None)                 # order NULL
+    assert lib.twell_partition_overflow(GOOD, GOOD, 64, ctypes.byref(noo), None) == -1
+    odd = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD + 2)             # order misaligned
+    assert lib.twell_partition_overflow(GOOD, GOOD, 64, ctypes.byref(odd), None) == -2
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, None, None) == -1
     assert lib.twell_ffn_hybrid_workspace_bytes(0, 512, 64, 1) == 0
 

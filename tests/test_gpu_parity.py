@@ -89,6 +89,7 @@ EDGE = [
     (512, 256, 1024, 128, 3, "bf16", 0.4, 0.2, 0),     # nearly every row overflows
     (200, 256, 1024, 256, 64, "bf16", 0.3, 0.5, 0),    # large cap (staging beyond LDS: general epilogue)
     (96, 128, 512, 64, 48, "f32", 0.4, 0.5, 0),        # fp32, large cap, w = 64
+    (20000, 64, 256, 64, 4, "bf16", 0.05, 0.8, 0),     # T > 16384: a second partition chunk
 ]
 
 

@@ -37,7 +37,7 @@ class TwellT(ctypes.Structure):
 class TwellHybridT(ctypes.Structure):
     _fields_ = [("ell", TwellT), ("max_ovf", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("row_ovf", ctypes.c_void_p), ("ovf_rows", ctypes.c_void_p), ("n_ovf", ctypes.c_void_p),
-                ("dense", ctypes.c_void_p)]
+                ("dense", ctypes.c_void_p), ("order", ctypes.c_void_p)]
 
 
 class TwellError(RuntimeError):
@@ -63,7 +63,7 @@ def load(path: str = LIB_PATH):
     lib.twell_pack_gate.argtypes = [P, P, I32, ctypes.POINTER(TwellT), P]
     lib.twell_partition_overflow.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
     lib.twell_pack_gate_hybrid.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
-    lib.twell_ffn_fused.argtypes = [ctypes.POINTER(TwellT), P, P, P, I32, P, P]
+    lib.twell_ffn_fused.argtypes = [ctypes.POINTER(TwellT), P, P, P, P, I32, P, P]
     lib.twell_ffn_hybrid_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.twell_ffn_hybrid_workspace_bytes.restype = ctypes.c_size_t
     lib.twell_ffn_hybrid.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
@@ -143,6 +143,7 @@ class Hybrid:
     ovf_rows: object  # [max_ovf] int32
     n_ovf: object     # [1] int32
     dense: object     # [max_ovf][F] dtype
+    order: object     # [T] int32: the fused step's work order
 
     @classmethod
     def empty(cls, T, F, tile_w, cap, dtype, max_ovf, device="cuda"):
@@ -151,11 +152,12 @@ class Hybrid:
                    torch.empty(T, dtype=torch.int32, device=device),
                    torch.empty(max(max_ovf, 1), dtype=torch.int32, device=device),
                    torch.empty(1, dtype=torch.int32, device=device),
-                   torch.empty((max(max_ovf, 1), F), dtype=dtype, device=device))
+                   torch.empty((max(max_ovf, 1), F), dtype=dtype, device=device),
+                   torch.empty(T, dtype=torch.int32, device=device))
 
     def desc(self) -> TwellHybridT:
         return TwellHybridT(self.ell.desc(), self.max_ovf, 0, _ptr(self.row_ovf), _ptr(self.ovf_rows),
-                            _ptr(self.n_ovf), _ptr(self.dense))
+                            _ptr(self.n_ovf), _ptr(self.dense), _ptr(self.order))
 
 
 # ---------------------------------------------------------------- the C entry points
@@ -179,10 +181,10 @@ def twell_pack_gate_hybrid(x, wg_t, hy: Hybrid, stream=None):
                                       _stream(stream)))
 
 
-def twell_ffn_fused(tw: TwELL, x, wu_t, wd, y, stream=None):
+def twell_ffn_fused(tw: TwELL, x, wu_t, wd, y, stream=None, order=None):
     lib = load()
-    _check("twell_ffn_fused", lib.twell_ffn_fused(ctypes.byref(tw.desc()), _ptr(x), _ptr(wu_t), _ptr(wd),
-                                                  int(x.shape[1]), _ptr(y), _stream(stream)))
+    _check("twell_ffn_fused", lib.twell_ffn_fused(ctypes.byref(tw.desc()), _ptr(order), _ptr(x), _ptr(wu_t),
+                                                  _ptr(wd), int(x.shape[1]), _ptr(y), _stream(stream)))
 
 
 def twell_ffn_hybrid_workspace_bytes(max_ovf: int, F: int, d: int, dtype) -> int:

@@ -66,14 +66,14 @@ int check_hybrid(const twell_hybrid_t *hy)
         return TWELL_E_SHAPE;
     if (hy->ell.T == 0)
         return TWELL_OK;
-    if (!hy->row_ovf || !hy->n_ovf)
+    if (!hy->row_ovf || !hy->n_ovf || !hy->order)
         return TWELL_E_NULL;
     if (hy->max_ovf > 0 && (!hy->ovf_rows || !hy->dense))
         return TWELL_E_NULL;
     if (hy->max_ovf > 0 && !aligned16(hy->dense))
         return TWELL_E_ALIGN;
     if ((reinterpret_cast<uintptr_t>(hy->row_ovf) & 3u) || (reinterpret_cast<uintptr_t>(hy->ovf_rows) & 3u) ||
-        (reinterpret_cast<uintptr_t>(hy->n_ovf) & 3u))
+        (reinterpret_cast<uintptr_t>(hy->n_ovf) & 3u) || (reinterpret_cast<uintptr_t>(hy->order) & 3u))
         return TWELL_E_ALIGN;
     return TWELL_OK;
 }
@@ -148,8 +148,9 @@ int twell_partition_overflow(const void *x, const void *wg_t, int32_t d, const t
         return TWELL_E_NULL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int n_b = h->F / h->tile_w;
-    TWELL_TRY(hip_status(twell::launch_row_flags(h->cnt, h->T, n_b, h->cap, hy->row_ovf, s)));
-    TWELL_TRY(hip_status(twell::launch_compact_rows(hy->row_ovf, h->T, hy->max_ovf, hy->ovf_rows, hy->n_ovf, s)));
+    TWELL_TRY(hip_status(twell::launch_row_flags(h->cnt, h->T, n_b, h->cap, hy->row_ovf, hy->order, s)));
+    TWELL_TRY(hip_status(
+        twell::launch_compact_rows(hy->row_ovf, h->T, hy->max_ovf, hy->ovf_rows, hy->n_ovf, hy->order, s)));
     return hip_status(twell::launch_dense_gate(h->vdtype, x, h->T, wg_t, hy->ovf_rows, hy->n_ovf, hy->max_ovf, d, h->F,
                                                hy->dense, s));
 }
@@ -164,8 +165,8 @@ int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d, const twe
     return twell_partition_overflow(x, wg_t, d, hy, stream);
 }
 
-int twell_ffn_fused(const twell_t *h, const void *x, const void *wu_t, const void *wd, int32_t d, float *y,
-                    void *stream)
+int twell_ffn_fused(const twell_t *h, const int32_t *order, const void *x, const void *wu_t, const void *wd,
+                    int32_t d, float *y, void *stream)
 {
     TWELL_TRY(check_layout(h, d));
     if (h->T == 0)
@@ -175,8 +176,10 @@ int twell_ffn_fused(const twell_t *h, const void *x, const void *wu_t, const voi
     TWELL_TRY(check_mat(wu_t));
     TWELL_TRY(check_mat(wd));
     TWELL_TRY(check_mat(y));
-    return hip_status(twell::launch_ffn_fused(h->vdtype, h->cnt, h->val, h->idx, h->T, h->F, h->tile_w, h->cap, x,
-                                              wu_t, wd, d, y, static_cast<hipStream_t>(stream)));
+    if (reinterpret_cast<uintptr_t>(order) & 3u)
+        return TWELL_E_ALIGN;
+    return hip_status(twell::launch_ffn_fused(h->vdtype, h->cnt, h->val, h->idx, order, h->T, h->F, h->tile_w,
+                                              h->cap, x, wu_t, wd, d, y, static_cast<hipStream_t>(stream)));
 }
 
 size_t twell_ffn_hybrid_workspace_bytes(int32_t max_ovf, int32_t F, int32_t d, int32_t vdtype)
@@ -236,7 +239,7 @@ int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, 
         return TWELL_E_WORKSPACE;
     if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return TWELL_E_ALIGN;
-    TWELL_TRY(twell_ffn_fused(h, x, wu_t, wd, d, y, stream));
+    TWELL_TRY(twell_ffn_fused(h, hy->order, x, wu_t, wd, d, y, stream));
     return twell_ffn_overflow(hy, x, wu_t, wd, d, y, workspace, workspace_bytes, stream);
 }
 

@@ -6,7 +6,9 @@
 // only the weights it needs (column j of W_u, row j of W_d), takes a dot
 // product and a scalar product, and accumulates -- DRAM traffic is the point.
 //
-// gfx950 mapping: one workgroup of 4 waves per token.  Each wave keeps the
+// gfx950 mapping: one workgroup of 4 waves per token, started in a given
+// work order (tokens with the most entries first, so that they do not trail
+// at the end of the launch while the light ones have long finished).  Each wave keeps the
 // token's x row and a partial y row in registers (chunk c of lane l covers
 // elements (l + 64c)*E .. +E, so every weight-row read is one fully coalesced
 // 16-byte-per-lane sweep).  The token's TwELL entries are compacted into an LDS
@@ -34,6 +36,7 @@ template <typename TI> struct FusedArgs {
     const int32_t *cnt;
     const TI *val;
     const uint8_t *idx;
+    const int32_t *order;  // row of workgroup i (null: row i)
     int T, n_b, tile_w, cap, F;
     const TI *x, *wu_t, *wd;
     int d, nchunks;  // nchunks = 16-byte chunks per row
@@ -175,7 +178,12 @@ __global__ __launch_bounds__(64 * NWV) void ffn_fused_kernel(FusedArgs<TI> a)
     __shared__ __attribute__((aligned(16))) float part[NWV][YW];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t = blockIdx.x;
+    int t = blockIdx.x;
+    if (a.order) {
+        t = a.order[t];
+        if ((unsigned)t >= (unsigned)a.T)
+            return;  // not a permutation: this row is not ours to write
+    }
     const int64_t row_bytes = (int64_t)a.d * Elt<TI>::SIZE;
     float *yrow = a.y + (int64_t)t * a.d;
 
@@ -299,11 +307,11 @@ static hipError_t fused_go(const FusedArgs<TI> &a, hipStream_t s)
 }
 
 template <typename TI>
-static hipError_t fused_dispatch(const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F, int tile_w,
-                                 int cap, const void *x, const void *wu_t, const void *wd, int d, float *y,
-                                 hipStream_t s)
+static hipError_t fused_dispatch(const int32_t *cnt, const void *val, const uint8_t *idx, const int32_t *order,
+                                 int T, int F, int tile_w, int cap, const void *x, const void *wu_t, const void *wd,
+                                 int d, float *y, hipStream_t s)
 {
-    FusedArgs<TI> a{cnt, static_cast<const TI *>(val), idx, T, F / tile_w, tile_w, cap, F,
+    FusedArgs<TI> a{cnt, static_cast<const TI *>(val), idx, order, T, F / tile_w, tile_w, cap, F,
                     static_cast<const TI *>(x), static_cast<const TI *>(wu_t), static_cast<const TI *>(wd),
                     d, (int)((int64_t)d * Elt<TI>::SIZE / 16), y};
     const int nch = a.nchunks;
@@ -316,13 +324,13 @@ static hipError_t fused_dispatch(const int32_t *cnt, const void *val, const uint
     return fused_go<TI, 8>(a, s);
 }
 
-hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F,
-                            int tile_w, int cap, const void *x, const void *wu_t, const void *wd, int d, float *y,
-                            hipStream_t s)
+hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, const int32_t *order,
+                            int T, int F, int tile_w, int cap, const void *x, const void *wu_t, const void *wd, int d,
+                            float *y, hipStream_t s)
 {
     if (vdtype == 1)
-        return fused_dispatch<__bf16>(cnt, val, idx, T, F, tile_w, cap, x, wu_t, wd, d, y, s);
-    return fused_dispatch<float>(cnt, val, idx, T, F, tile_w, cap, x, wu_t, wd, d, y, s);
+        return fused_dispatch<__bf16>(cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, s);
+    return fused_dispatch<float>(cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, s);
 }
 
 }  // namespace twell

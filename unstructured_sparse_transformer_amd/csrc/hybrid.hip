@@ -6,7 +6,8 @@
 // Steps on the device, all on the caller's stream with no host round trip:
 //   row_flags     row_ovf[t] = some tile of row t has cnt > cap
 //   compact_rows  one workgroup turns the flags into the ascending overflow-row
-//                 list and its length (workgroup prefix sum, no atomics)
+//                 list and its length (workgroup prefix sum, no atomics), and
+//                 the rows' entry counts into the fused step's work order
 //   dense_gate    ReLU(x . W_g) for the listed rows  -> dense backup
 //   gated_up      round(dense * (x . W_u))  for the listed rows -> workspace
 //   down          (gated product) . W_d     -> y rows of the listed tokens
@@ -19,95 +20,191 @@ namespace twell {
 
 // ------------------------------------------------------------------ partition
 // One thread per row; VEC: the row's counts are read as 16-byte vectors.
+// work[t] = stored entries of row t, sum over tiles of min(cnt, cap), or 0
+// for an overflow row (its fused-step work is a row of zeros).
 template <bool VEC>
 __global__ __launch_bounds__(256) void row_flags_kernel(const int32_t *__restrict__ cnt, int T, int n_b, int cap,
-                                                        int32_t *__restrict__ row_ovf)
+                                                        int32_t *__restrict__ row_ovf, int32_t *__restrict__ work)
 {
     const int t = blockIdx.x * 256 + threadIdx.x;
     if (t >= T)
         return;
     const int32_t *c = cnt + (int64_t)t * n_b;
-    int f = 0;
+    int f = 0, e = 0;
     if constexpr (VEC) {
         for (int b = 0; b < n_b; b += 4) {
             const int4 v = *reinterpret_cast<const int4 *>(c + b);
             f |= (v.x > cap) | (v.y > cap) | (v.z > cap) | (v.w > cap);
+            e += min(v.x, cap) + min(v.y, cap) + min(v.z, cap) + min(v.w, cap);
         }
     } else {
-        for (int b = 0; b < n_b; ++b)
+        for (int b = 0; b < n_b; ++b) {
             f |= c[b] > cap;
+            e += min(c[b], cap);
+        }
     }
     row_ovf[t] = f;
+    work[t] = f ? 0 : e;
 }
 
-// One workgroup: thread i owns rows [base + 16 i, base + 16 i + 16) of each
-// 16384-row chunk; per-thread counts -> workgroup exclusive scan (ballot-free
-// wave scan + 16 wave totals in LDS) -> each thread writes its flagged rows in
-// ascending order.  n_ovf is the true number of flagged rows.
-constexpr int CR_THREADS = 1024, CR_ROWS = 16;
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (lanes shifted in from outside a row contribute 0).
+__device__ __forceinline__ int wave_incl_scan_dpp(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+// Work classes of the fused step's schedule, heaviest = 7.
+__device__ __forceinline__ int work_class(int e)
+{
+    return e == 0 ? 0 : e < 16 ? 1 : e < 32 ? 2 : e < 64 ? 3 : e < 128 ? 4 : e < 192 ? 5 : e < 256 ? 6 : 7;
+}
+
+// One workgroup, per chunk of 16384 rows: the rows' flags and work classes
+// are read with coalesced loads into a byte per row in LDS; thread i then
+// owns rows [16 i, 16 i + 16) of the chunk.  Nine per-thread counts (flagged
+// rows; rows of each work class) go through one workgroup exclusive scan (DPP
+// wave scans + 16 wave totals in LDS); each thread writes its flagged rows to
+// the ascending overflow list and its rows to their places in the chunk's
+// work order (classes from the heaviest, ascending rows inside a class),
+// staged in LDS and written out coalesced.  `order` holds the rows' work
+// values on entry; each chunk reads all of its values before the first
+// barrier and writes only its own positions after it.  n_ovf is the true
+// number of flagged rows.
+constexpr int CR_THREADS = 1024, CR_ROWS = 16, CR_NC = 8, CR_CHUNK = CR_THREADS * CR_ROWS;
 
 __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t *__restrict__ row_ovf, int T,
                                                                   int max_ovf, int32_t *__restrict__ ovf_rows,
-                                                                  int32_t *__restrict__ n_ovf)
+                                                                  int32_t *__restrict__ n_ovf, int32_t *order)
 {
-    __shared__ int wave_tot[CR_THREADS / 64];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    constexpr int NV = CR_NC + 1;  // scanned values: classes 0..7, flagged rows
+    constexpr int NW = CR_THREADS / 64;
+    __shared__ int wave_tot[NW][NV];
+    __shared__ int wave_off[NW + 1][NV];  // exclusive prefix over waves; row NW = totals
+    __shared__ __attribute__((aligned(16))) uint8_t srow[CR_CHUNK];  // bit 7: flagged; bits 0-2: class
+    __shared__ int sord[CR_CHUNK];                                   // the chunk's work order
+    const int tid = threadIdx.x, wave = tid >> 6;
     int base = 0;
-    for (int t0 = 0; t0 < T; t0 += CR_THREADS * CR_ROWS) {
-        const int r0 = t0 + tid * CR_ROWS;
+    for (int t0 = 0; t0 < T; t0 += CR_CHUNK) {
+        const int nrows = T - t0 < CR_CHUNK ? T - t0 : CR_CHUNK;
+#pragma unroll 4
+        for (int k = 0; k < CR_ROWS; ++k) {
+            const int i = k * CR_THREADS + tid;
+            if (i < nrows)
+                srow[i] = (uint8_t)((row_ovf[t0 + i] != 0 ? 0x80 : 0) | work_class(order[t0 + i]));
+        }
+        __syncthreads();
+        const int i0 = tid * CR_ROWS;
+        const u32x4 rb = *reinterpret_cast<const u32x4 *>(srow + i0);
         uint32_t bits = 0;
+        uint64_t cls = 0;   // 4 bits per row: its work class
+        uint64_t ccnt = 0;  // 8 bits per class: rows of this thread in it
 #pragma unroll
         for (int k = 0; k < CR_ROWS; ++k) {
-            const int t = r0 + k;
-            bits |= (t < T && row_ovf[t] != 0) ? (1u << k) : 0u;
+            if (i0 + k < nrows) {
+                const uint32_t by = (rb[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                bits |= (by & 0x80u) ? (1u << k) : 0u;
+                const uint32_t c = by & 7u;
+                cls |= (uint64_t)c << (4 * k);
+                ccnt += 1ull << (8 * c);
+            }
         }
-        const int mine = __popc(bits);
-        int incl = mine;
+        int mine[NV], incl[NV];
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int u = __shfl_up(incl, o, 64);
-            if (lane >= o)
-                incl += u;
+        for (int v = 0; v < CR_NC; ++v)
+            mine[v] = (int)((ccnt >> (8 * v)) & 0xFFu);
+        mine[CR_NC] = __popc(bits);
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            incl[v] = wave_incl_scan_dpp(mine[v]);
+        if ((tid & 63) == 63) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                wave_tot[wave][v] = incl[v];
         }
-        if (lane == 63)
-            wave_tot[wave] = incl;
         __syncthreads();
-        int off = 0, tot = 0;
-#pragma unroll
-        for (int w = 0; w < CR_THREADS / 64; ++w) {
-            const int c = wave_tot[w];
-            off += w < wave ? c : 0;
-            tot += c;
+        if (tid < NW * NV) {
+            const int w = tid / NV, v = tid - w * NV;
+            int off = 0;
+            for (int q = 0; q < w; ++q)
+                off += wave_tot[q][v];
+            wave_off[w][v] = off;
+            if (w == NW - 1)
+                wave_off[NW][v] = off + wave_tot[w][v];
         }
-        int pos = base + off + incl - mine;
-        while (bits) {
-            const int k = __ffs(bits) - 1;
-            bits &= bits - 1;
+        __syncthreads();
+        int start[NV], tot[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            start[v] = wave_off[wave][v] + incl[v] - mine[v];  // this thread's first position inside value v
+            tot[v] = wave_off[NW][v];
+        }
+        // overflow list
+        int pos = base + start[CR_NC];
+        uint32_t bb = bits;
+        while (bb) {
+            const int k = __ffs(bb) - 1;
+            bb &= bb - 1;
             if (pos < max_ovf)
-                ovf_rows[pos] = r0 + k;
+                ovf_rows[pos] = t0 + i0 + k;
             ++pos;
         }
-        base += tot;
+        // work order: class c starts after all rows of the heavier classes
+        int cpos[CR_NC];
+        int above = 0;
+#pragma unroll
+        for (int c = CR_NC - 1; c >= 0; --c) {
+            cpos[c] = above + start[c];
+            above += tot[c];
+        }
+        uint64_t used = 0;  // 8 bits per class: rows placed so far
+#pragma unroll
+        for (int k = 0; k < CR_ROWS; ++k) {
+            if (i0 + k < nrows) {
+                const int c = (int)((cls >> (4 * k)) & 0xFu);
+                int p = 0;
+#pragma unroll
+                for (int q = 0; q < CR_NC; ++q)
+                    p = c == q ? cpos[q] : p;
+                sord[p + (int)((used >> (8 * c)) & 0xFFu)] = t0 + i0 + k;
+                used += 1ull << (8 * c);
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < CR_ROWS; ++k) {
+            const int i = k * CR_THREADS + tid;
+            if (i < nrows)
+                order[t0 + i] = sord[i];
+        }
+        base += tot[CR_NC];
         __syncthreads();
     }
     if (tid == 0)
         n_ovf[0] = base;
 }
 
-hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, hipStream_t s)
+hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, int32_t *work,
+                            hipStream_t s)
 {
     const bool vec = (n_b % 4 == 0) && ((reinterpret_cast<uintptr_t>(cnt) & 15u) == 0);
     if (vec)
-        row_flags_kernel<true><<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, T, n_b, cap, row_ovf);
+        row_flags_kernel<true><<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, T, n_b, cap, row_ovf, work);
     else
-        row_flags_kernel<false><<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, T, n_b, cap, row_ovf);
+        row_flags_kernel<false><<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, T, n_b, cap, row_ovf, work);
     return hipGetLastError();
 }
 
 hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows, int32_t *n_ovf,
-                               hipStream_t s)
+                               int32_t *order, hipStream_t s)
 {
-    compact_rows_kernel<<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf);
+    compact_rows_kernel<<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
     return hipGetLastError();
 }
 

@@ -11,12 +11,15 @@ namespace twell {
 hipError_t launch_gate_twell(int vdtype, const void *x, const void *wg_t, int T, int d, int F, int tile_w,
                              int cap, void *val, uint8_t *idx, int32_t *cnt, hipStream_t s);
 
-// row_ovf[t] = any tile of row t has cnt > cap.
-hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, hipStream_t s);
+// row_ovf[t] = any tile of row t has cnt > cap; work[t] = stored entries of
+// row t (0 for an overflow row).
+hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, int32_t *work,
+                            hipStream_t s);
 
-// Ascending list of flagged rows (first max_ovf of them) and their total count.
+// Ascending list of flagged rows (first max_ovf of them) and their total
+// count; `order` holds the work values on entry and the work order on return.
 hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows, int32_t *n_ovf,
-                               hipStream_t s);
+                               int32_t *order, hipStream_t s);
 
 // dense[i][:] = ReLU(x[ovf_rows[i]] . W_g) for i < min(*n_ovf, max_ovf).
 hipError_t launch_dense_gate(int vdtype, const void *x, int T, const void *wg_t, const int32_t *ovf_rows,
@@ -32,10 +35,11 @@ hipError_t launch_gated_up(int vdtype, const void *x, int T, const void *wu_t, c
 hipError_t launch_down(int vdtype, const void *p, const void *wd, const int32_t *ovf_rows, const int32_t *n_ovf,
                        int max_ovf, int F, int d, float *y, float *part, int splits, hipStream_t s);
 
-// Fused up/down from TwELL for every row (overflow rows -> 0).
-hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F,
-                            int tile_w, int cap, const void *x, const void *wu_t, const void *wd, int d, float *y,
-                            hipStream_t s);
+// Fused up/down from TwELL for every row (overflow rows -> 0); workgroup i
+// handles row order[i] (row i when order is null).
+hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, const int32_t *order,
+                            int T, int F, int tile_w, int cap, const void *x, const void *wu_t, const void *wd, int d,
+                            float *y, hipStream_t s);
 
 // Number of split-K slabs the hybrid down projection uses for these sizes.
 int down_splits(int max_ovf, int F, int d);
