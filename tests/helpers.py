@@ -30,7 +30,20 @@ def to_device(wl):
     return dt, f(wl.x), f(wl.wg_t), f(wl.wu_t), f(wl.wd)
 
 
-def run_hip(wl, max_ovf=None, stream=None):
+def _offset_views(hy, dt):
+    """Re-point the TwELL buffers at views that start one element into larger
+    allocations (val: 2 or 4 bytes, idx: 1 byte, cnt: 4 bytes off 16-byte
+    alignment), so the kernels' scalar (unaligned) paths run."""
+    import torch
+    ell = hy.ell
+    nv = ell.val.numel()
+    ell.val = torch.empty(nv + 8, dtype=dt, device="cuda")[1:1 + nv].view(ell.val.shape)
+    ell.idx = torch.empty(nv + 16, dtype=torch.uint8, device="cuda")[1:1 + nv].view(ell.idx.shape)
+    nc = ell.cnt.numel()
+    ell.cnt = torch.empty(nc + 4, dtype=torch.int32, device="cuda")[1:1 + nc].view(ell.cnt.shape)
+
+
+def run_hip(wl, max_ovf=None, stream=None, unaligned=False):
     """Run pack_gate_hybrid + ffn_hybrid and (separately) ffn_fused; return host arrays."""
     import torch
     import unstructured_sparse_transformer_amd as tw
@@ -38,6 +51,8 @@ def run_hip(wl, max_ovf=None, stream=None):
     if max_ovf is None:
         max_ovf = wl.T
     hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
+    if unaligned:
+        _offset_views(hy, dt)
     # poison the outputs so stale memory cannot pass a check
     hy.ell.cnt.fill_(-7)
     hy.ell.idx.fill_(0xAB)

@@ -102,6 +102,19 @@ def test_edge_shapes(gpu_lib, case):
     compare(wl, out, label=wl.name)
 
 
+@pytest.mark.parametrize("case", [(300, 256, 1024, 256, 16, "bf16"), (200, 128, 512, 64, 8, "bf16"),
+                                  (100, 128, 512, 128, 16, "f32")],
+                         ids=["w256_c16_bf16", "w64_c8_bf16", "w128_c16_f32"])
+def test_unaligned_twell_buffers(gpu_lib, case):
+    """val / idx / cnt one element off 16-byte alignment: the scalar store and
+    load paths of the epilogue, the partition and the fused step."""
+    T, d, F, w, cap, dt = case
+    wl = make_random_small(T, d, F, w, cap, dt, active_frac=0.06, seed=T + w, jitter=0.6)
+    say(f"case unaligned TwELL buffers {wl.name}")
+    out = run_hip(wl, unaligned=True)
+    compare(wl, out, label=f"unaligned {wl.name}")
+
+
 def test_all_dead(gpu_lib):
     wl = make_random_small(200, 256, 1024, 256, 16, "bf16", active_frac=0.3, seed=11)
     wl.wg_t[:, -1] = -np.inf
