@@ -240,39 +240,44 @@ __device__ __forceinline__ int rows_used(const GemmArgs &p)
 }
 
 // MODE 0: out = ReLU(acc) (dense backup).  MODE 1: out = round(gate * acc).
+// The grid is at most one workgroup per CU; workgroup g takes output tiles
+// t = g, g + gridDim.x, ... of the tiles that cover the rows in use (M tiles
+// slowest), so no workgroup is launched for rows past n_ovf.  With the grid
+// and the N-tile count multiples of 8, every tile of one N column (one B
+// tile) lands on the same XCD.
 template <typename TI, int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dense_epi_kernel(GemmArgs p, DenseOut<TI> o)
 {
     using Core = GemmCore<TI, BM, BN, WM, WN, false, HB_KB, HB_STAGES>;
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
     const int m_used = rows_used(p);
-    int mt, nt;
-    tile_coords(blockIdx.x, p.MT, p.NT, mt, nt);
-    const int m0 = mt * BM, n0 = nt * BN;
-    if (m0 >= m_used)
-        return;
-    Core core;
-    f32x16 acc[Core::FM][Core::FN];
-    core.run(p, smem, m0, n0, m_used, p.k_begin, p.k_len, threadIdx.x, acc);
+    const int ntiles = (m_used + BM - 1) / BM * p.NT;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / Core::NWN, wn = wave % Core::NWN;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int nt = t % p.NT, mt = t / p.NT;
+        const int m0 = mt * BM, n0 = nt * BN;
+        Core core;
+        f32x16 acc[Core::FM][Core::FN];
+        core.run(p, smem, m0, n0, m_used, p.k_begin, p.k_len, tid, acc);
 #pragma unroll
-    for (int fm = 0; fm < Core::FM; ++fm)
+        for (int fm = 0; fm < Core::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < Core::FN; ++fn)
+            for (int fn = 0; fn < Core::FN; ++fn)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
-                const int n = n0 + wn * WN + fn * 32 + (lane & 31);
-                if (m < m_used && n < p.N) {
-                    const int64_t off = (int64_t)m * p.N + n;
-                    const float v = acc[fm][fn][i];
-                    if (MODE == 0)
-                        store_elem(o.out + off, v > 0.f ? v : 0.f);
-                    else
-                        store_elem(o.out + off, load_elem(o.gate + off) * v);
+                for (int i = 0; i < 16; ++i) {
+                    const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
+                    const int n = n0 + wn * WN + fn * 32 + (lane & 31);
+                    if (m < m_used && n < p.N) {
+                        const int64_t off = (int64_t)m * p.N + n;
+                        const float v = acc[fm][fn][i];
+                        if (MODE == 0)
+                            store_elem(o.out + off, v > 0.f ? v : 0.f);
+                        else
+                            store_elem(o.out + off, load_elem(o.gate + off) * v);
+                    }
                 }
-            }
+    }
 }
 
 template <typename TI> struct DownOut {
@@ -282,38 +287,40 @@ template <typename TI> struct DownOut {
     int splits;
 };
 
+// Same tile loop as dense_epi_kernel over (M tile, split, N tile), N tile fastest.
 template <typename TI, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void down_kernel(GemmArgs p, DownOut<TI> o)
 {
     using Core = GemmCore<TI, BM, BN, WM, WN, true, DN_KB, DN_STAGES>;
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
     const int m_used = rows_used(p);
-    int mt, nt;
-    tile_coords(blockIdx.x, p.MT, p.NT, mt, nt);
-    const int m0 = mt * BM, n0 = nt * BN;
-    if (m0 >= m_used)
-        return;
-    const int sidx = blockIdx.y;
-    Core core;
-    f32x16 acc[Core::FM][Core::FN];
-    core.run(p, smem, m0, n0, m_used, p.k_begin + sidx * p.k_split_len, p.k_split_len, threadIdx.x, acc);
+    const int per_m = p.NT * o.splits;
+    const int ntiles = (m_used + BM - 1) / BM * per_m;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / Core::NWN, wn = wave % Core::NWN;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int mt = t / per_m, u = t - mt * per_m;
+        const int sidx = u / p.NT, nt = u - sidx * p.NT;
+        const int m0 = mt * BM, n0 = nt * BN;
+        Core core;
+        f32x16 acc[Core::FM][Core::FN];
+        core.run(p, smem, m0, n0, m_used, p.k_begin + sidx * p.k_split_len, p.k_split_len, tid, acc);
 #pragma unroll
-    for (int fm = 0; fm < Core::FM; ++fm)
+        for (int fm = 0; fm < Core::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < Core::FN; ++fn)
+            for (int fn = 0; fn < Core::FN; ++fn)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
-                const int n = n0 + wn * WN + fn * 32 + (lane & 31);
-                if (m < m_used && n < p.N) {
-                    if (o.splits == 1)
-                        o.y[(int64_t)o.rows[m] * p.N + n] = acc[fm][fn][i];
-                    else
-                        o.part[((int64_t)sidx * p.M + m) * p.N + n] = acc[fm][fn][i];
+                for (int i = 0; i < 16; ++i) {
+                    const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
+                    const int n = n0 + wn * WN + fn * 32 + (lane & 31);
+                    if (m < m_used && n < p.N) {
+                        if (o.splits == 1)
+                            o.y[(int64_t)o.rows[m] * p.N + n] = acc[fm][fn][i];
+                        else
+                            o.part[((int64_t)sidx * p.M + m) * p.N + n] = acc[fm][fn][i];
+                    }
                 }
-            }
+    }
 }
 
 // y[rows[m]][n] = sum over splits s (in order) of part[s][m][n].
@@ -347,6 +354,19 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 constexpr int HB_BM = 64, HB_WM = 32;
 constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32, DN_WN = 128;
 
+// Workgroups for a tile loop: one per CU, at most `tiles`, rounded down to a
+// multiple of 8 when that many (keeps N columns on one XCD).
+static int loop_grid(long tiles)
+{
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    long g = tiles < ncu ? tiles : ncu;
+    if (g >= 8)
+        g &= ~7L;
+    return (int)(g > 0 ? g : 1);
+}
+
 template <typename TI, int MODE>
 static hipError_t dense_go(const void *x, int T, const void *w_t, const int32_t *ovf_rows, const int32_t *n_ovf,
                            int max_ovf, int d, int F, const void *gate, void *out, hipStream_t s)
@@ -370,7 +390,7 @@ static hipError_t dense_go(const void *x, int T, const void *w_t, const int32_t 
     p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
     DenseOut<TI> o{static_cast<TI *>(out), static_cast<const TI *>(gate)};
     dense_epi_kernel<TI, HB_BM, HB_BN, HB_WM, HB_WN, MODE>
-        <<<dim3(p.MT * p.NT), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);
+        <<<dim3(loop_grid((long)p.MT * p.NT)), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);
     return hipGetLastError();
 }
 
@@ -426,11 +446,11 @@ static hipError_t down_go(const void *pbuf, const void *wd, const int32_t *ovf_r
     p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
     DownOut<TI> o{part, y, ovf_rows, splits};
     down_kernel<TI, DN_BM, DN_BN, DN_WM, DN_WN>
-        <<<dim3(p.MT * p.NT, splits), dim3((DN_BM / DN_WM) * (DN_BN / DN_WN) * 64), 0, s>>>(p, o);
+        <<<dim3(loop_grid((long)p.MT * p.NT * splits)), dim3((DN_BM / DN_WM) * (DN_BN / DN_WN) * 64), 0, s>>>(p, o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;
-    split_reduce_kernel<<<dim3((d / 4 + 255) / 256, max_ovf < 4096 ? max_ovf : 4096), dim3(256), 0, s>>>(part, splits, max_ovf, n_ovf, d,
+    split_reduce_kernel<<<dim3((d / 4 + 255) / 256, max_ovf < 512 ? max_ovf : 512), dim3(256), 0, s>>>(part, splits, max_ovf, n_ovf, d,
                                                                              ovf_rows, y);
     return hipGetLastError();
 }
