@@ -193,6 +193,20 @@ struct GemmCore {
     static_assert(!B_KN || (1024 % RAW_ROW == 0 && (KT / RAW_RPI) % NW == 0), "raw B rows split over the waves");
     static_assert(!B_KN || B_UNITS % NTHR == 0 || B_UNITS < NTHR, "transpose blocks split over the threads");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is whole 32x32 blocks");
+    static_assert(!B_KN || KB == 128, "the transposed B tile's swizzle assumes 128-byte rows");
+
+    // LDS byte offset of (row, 16-byte chunk) in the B operand tile.  NK: the
+    // copy layout.  KN (written by transpose_b): the chunk is XOR-ed with bits
+    // 1-3 of the row and bits 4-6, so that both the fragment reads (16
+    // consecutive rows) and the transposing stores (rows 8 apart, both
+    // parities) of a 16-lane phase hit 16 distinct 16-byte bank groups.
+    __device__ __forceinline__ static int b_off(int row, int chunk)
+    {
+        if constexpr (B_KN)
+            return row * KB + ((chunk ^ (((row >> 1) ^ (row >> 4)) & 7)) << 4);
+        else
+            return lds_off<KB>(row, chunk);
+    }
 
     __amdgpu_buffer_rsrc_t ra, rb;
     int a_voff[A_LD];
@@ -277,9 +291,9 @@ struct GemmCore {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     rr[e] = *reinterpret_cast<const u32x4 *>(raw + (kg * E + e) * RAW_ROW + ng * 16);
+                u32x4 o[E];  // o[n]: column n of the block, its E k values
 #pragma unroll
                 for (int n = 0; n < E; ++n) {
-                    u32x4 o;
                     if constexpr (SZ == 2) {
 #pragma unroll
                         for (int w = 0; w < 4; ++w) {
@@ -287,14 +301,26 @@ struct GemmCore {
                             const uint32_t hi = rr[2 * w + 1][n >> 1];
                             const uint32_t l16 = (n & 1) ? (lo >> 16) : (lo & 0xFFFFu);
                             const uint32_t h16 = (n & 1) ? (hi >> 16) : (hi & 0xFFFFu);
-                            o[w] = l16 | (h16 << 16);
+                            o[n][w] = l16 | (h16 << 16);
                         }
                     } else {
 #pragma unroll
                         for (int w = 0; w < 4; ++w)
-                            o[w] = rr[w][n];
+                            o[n][w] = rr[w][n];
                     }
-                    *reinterpret_cast<u32x4 *>(bop + lds_off<KB>(ng * E + n, kg)) = o;
+                }
+                // Odd n-groups write their columns in the order 1, 0, 3, 2, ...:
+                // each store then covers rows of both parities, which with the
+                // B-tile swizzle puts every 16-lane phase on 16 distinct bank groups.
+                const int odd = ng & 1;
+                const uint32_t msk = 0u - (uint32_t)odd;  // all ones for an odd n-group
+#pragma unroll
+                for (int q = 0; q < E; ++q) {
+                    u32x4 w;  // o[q ^ odd], as a bit blend (an indexed pick compiles to a select chain)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        w[i] = o[q][i] ^ ((o[q][i] ^ o[q ^ 1][i]) & msk);
+                    *reinterpret_cast<u32x4 *>(bop + b_off(ng * E + (q ^ odd), kg)) = w;
                 }
             }
         }
@@ -312,7 +338,7 @@ struct GemmCore {
             af[0][fm] = *reinterpret_cast<const u32x4 *>(sa + lds_off<KB>(wm * WM + fm * 32 + lr, lh));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-            bfr[0][fn] = *reinterpret_cast<const u32x4 *>(sb + lds_off<KB>(wn * WN + fn * 32 + lr, lh));
+            bfr[0][fn] = *reinterpret_cast<const u32x4 *>(sb + b_off(wn * WN + fn * 32 + lr, lh));
 #pragma unroll
         for (int ss = 0; ss < SUB; ++ss) {
             const int cb = ss & 1, nb = cb ^ 1;
@@ -324,7 +350,7 @@ struct GemmCore {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
                     bfr[nb][fn] = *reinterpret_cast<const u32x4 *>(
-                        sb + lds_off<KB>(wn * WN + fn * 32 + lr, (ss + 1) * 2 + lh));
+                        sb + b_off(wn * WN + fn * 32 + lr, (ss + 1) * 2 + lh));
             }
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
@@ -369,7 +395,7 @@ struct GemmCore {
             af[fm] = *reinterpret_cast<const u32x4 *>(sa + lds_off<KB>(wm * WM + fm * 32 + lr, ss * 2 + lh));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-            bf[fn] = *reinterpret_cast<const u32x4 *>(sb + lds_off<KB>(wn * WN + fn * 32 + lr, ss * 2 + lh));
+            bf[fn] = *reinterpret_cast<const u32x4 *>(sb + b_off(wn * WN + fn * 32 + lr, ss * 2 + lh));
     }
     __device__ __forceinline__ static void mfma_sub(const u32x4 (&af)[FM], const u32x4 (&bf)[FN],
                                                     f32x16 (&acc)[FM][FN])
