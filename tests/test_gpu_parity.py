@@ -90,6 +90,8 @@ EDGE = [
     (200, 256, 1024, 256, 64, "bf16", 0.3, 0.5, 0),    # large cap (staging beyond LDS: general epilogue)
     (96, 128, 512, 64, 48, "f32", 0.4, 0.5, 0),        # fp32, large cap, w = 64
     (20000, 64, 256, 64, 4, "bf16", 0.05, 0.8, 0),     # T > 16384: a second partition chunk
+    (50, 64, 64, 64, 8, "bf16", 0.1, 0.5, 0),          # F = 64: one tile, less than a gate N tile
+    (1, 128, 256, 32, 2, "f32", 0.3, 0.3, 0),          # T = 1, fp32
 ]
 
 
@@ -161,6 +163,19 @@ def test_overflow_beyond_max_ovf(gpu_lib):
     assert (num <= 1e-2 * np.linalg.norm(ref.y_exact[served], axis=1)).all()
     unserved = ref.ovf_local[16:]
     assert not out["y"][unserved].any()
+
+
+def test_max_ovf_zero(gpu_lib):
+    """max_ovf = 0: the partition still counts overflow rows; none gets a dense
+    row, and their y rows stay 0."""
+    wl = make_random_small(256, 128, 512, 128, 2, "bf16", active_frac=0.3, seed=16)
+    ref = oracle.reference(wl)
+    assert len(ref.ovf_local) > 0
+    say(f"case max_ovf=0 with n_ovf={len(ref.ovf_local)}")
+    out = run_hip(wl, max_ovf=0)
+    assert out["n_ovf"] == len(ref.ovf_local)
+    compare(wl, out, ref=ref, label="max_ovf=0")
+    assert not out["y"][ref.ovf_local].any()
 
 
 def test_zero_rows(gpu_lib):
