@@ -287,4 +287,6 @@ def make_workload(name: str, **kw) -> Workload:
         return WORKLOADS[name](**kw)
     if name.startswith("stress_l"):
         return make_stress_layer(int(name[len("stress_l"):]), **kw)
+    if name.startswith("decode_"):  # decode_<T>: the first T tokens of the 2B-like layer
+        return make_decode_windows(int(name[len("decode_"):]), max_windows=1)[0]
     raise KeyError(name)
