@@ -56,12 +56,22 @@ template <> struct StageWord<__bf16> {
         const __bf16 h = (__bf16)v;
         return (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)c << 16);
     }
+    // hi16: the column already shifted to bits 16..23
+    __device__ static W pack_hi(float v, uint32_t hi16)
+    {
+        const __bf16 h = (__bf16)v;
+        return (uint32_t)__builtin_bit_cast(uint16_t, h) | hi16;
+    }
     __device__ static uint32_t bits(W w) { return w & 0xFFFFu; }
     __device__ static uint32_t col(W w) { return w >> 16; }
 };
 template <> struct StageWord<float> {
     using W = uint64_t;
     __device__ static W pack(float v, int c) { return (uint64_t)__float_as_uint(v) | ((uint64_t)c << 32); }
+    __device__ static W pack_hi(float v, uint32_t hi16)
+    {
+        return (uint64_t)__float_as_uint(v) | ((uint64_t)(hi16 >> 16) << 32);
+    }
     __device__ static uint32_t bits(W w) { return (uint32_t)w; }
     __device__ static uint32_t col(W w) { return (uint32_t)(w >> 32); }
 };
@@ -315,7 +325,7 @@ __device__ __forceinline__ void twell_epilogue_seg(f32x16 (&acc)[WM / 32][WN / 3
 
     // pass A
     const int lc = lane & 31;
-    const uint32_t below = (1u << lc) - 1u;
+    const uint32_t lc16 = (uint32_t)lc << 16;
     const bool lo_half = lane < 32;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
@@ -336,12 +346,15 @@ __device__ __forceinline__ void twell_epilogue_seg(f32x16 (&acc)[WM / 32][WN / 3
                 const uint64_t b = __ballot(act);
                 const uint32_t blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
                 if (b != 0u) {
-                    const uint32_t half = lo_half ? blo : bhi;
-                    const int slot = (int)(lo_half ? pre_lo : pre_hi) + __popc(half & below);
+                    // pre + active lanes of this row below the lane: mbcnt counts the
+                    // set bits below the lane over all 64 lanes, so the upper half
+                    // starts from pre_hi minus the lower half's count.
+                    const int base = lo_half ? (int)pre_lo : (int)pre_hi - __popc(blo);
+                    const int slot = __builtin_amdgcn_mbcnt_hi(bhi, __builtin_amdgcn_mbcnt_lo(blo, base));
                     if (act && slot < cap) {
                         const int col = wn * WN + fn * 32;  // first column of the block in the workgroup
                         const int seg = col / SEGW;
-                        sw[(r * NSEG + seg) * cap + slot] = SW::pack(v, col % TW + lc);
+                        sw[(r * NSEG + seg) * cap + slot] = SW::pack_hi(v, ((uint32_t)(col % TW) << 16) | lc16);
                     }
                     pre_lo += __popc(blo);
                     pre_hi += __popc(bhi);
