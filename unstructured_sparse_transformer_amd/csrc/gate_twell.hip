@@ -9,10 +9,12 @@
 // On gfx950 the workgroup's N extent (256 columns) always covers whole TwELL
 // tiles, so the packing needs no cross-workgroup merge and is deterministic.
 // The epilogue works straight on the MFMA accumulators: one ballot per
-// accumulator register gives two rows' 32-column activity masks; their
-// popcounts go through LDS to form, per row and tile, the prefix over the
-// tile's 32-column blocks; each active lane then gets its slot as prefix +
-// popcount of the lower lanes of its row mask (ascending column order).
+// accumulator register gives two rows' activity over 32 columns, and each
+// active lane's slot is the count of active columns before it in its tile
+// (ascending column order).  Two forms: a single pass that fills per-wave
+// segments of each row's tile in LDS (the common case), and a four-pass form
+// (masks, per-row prefixes, placement, write-out) for capacities whose
+// staging would not fit in LDS.
 #include "launch.h"
 #include "twell_device.h"
 

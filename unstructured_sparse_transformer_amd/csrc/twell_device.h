@@ -17,12 +17,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#ifndef GEMM_IGLP
-#define GEMM_IGLP 0
-#endif
-#ifndef GEMM_PIPE
-#define GEMM_PIPE 1
-#endif
 
 namespace twell {
 
@@ -56,8 +50,6 @@ __device__ __forceinline__ void store_elem(__bf16 *p, float v) { *p = (__bf16)v;
 __device__ __forceinline__ void store_elem(float *p, float v) { *p = v; }
 __device__ __forceinline__ float load_elem(const __bf16 *p) { return (float)*p; }
 __device__ __forceinline__ float load_elem(const float *p) { return *p; }
-__device__ __forceinline__ float round_to_elem(__bf16, float v) { return (float)(__bf16)v; }
-__device__ __forceinline__ float round_to_elem(float, float v) { return v; }
 
 __device__ __forceinline__ u32x4 ldg16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
@@ -155,10 +147,6 @@ __device__ __forceinline__ void wg_barrier()
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
-
-// Wait until this wave's outstanding vector-memory operations (including the
-// global->LDS copies) and LDS operations have completed (vmcnt = lgkmcnt = 0).
-__device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
 template <typename TI, int BM, int BN, int WM, int WN, bool B_KN, int KB = 128, int STAGES = 2>
 struct GemmCore {
@@ -358,7 +346,6 @@ struct GemmCore {
                 for (int fn = 0; fn < FN; ++fn)
                     mfma_chunk(TI{}, af[cb][fm], bfr[cb][fn], acc[fm][fn]);
         }
-        __builtin_amdgcn_iglp_opt(GEMM_IGLP);
         // nothing of this stage may sink below the wait for the next stage's copies
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -473,14 +460,14 @@ struct GemmCore {
         __syncthreads();
     }
 
-    // Full K loop: an STAGES-deep ring of LDS slots fed by global->LDS copies
-    // issued STAGES-1 stages ahead; one barrier per stage (two for a KN B, whose
-    // stage is transposed in LDS first).  Ends with a barrier so the caller may
-    // reuse `smem`.
+    // Full K loop.  NK operands: run_nk.  KN B: an STAGES-deep ring of LDS
+    // slots fed by global->LDS copies issued STAGES-1 stages ahead, two
+    // barriers per stage (the stage is transposed in LDS first).  Ends with a
+    // barrier so the caller may reuse `smem`.
     __device__ __forceinline__ void run(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb, int klen,
                                         int tid, f32x16 (&acc)[FM][FN])
     {
-        if constexpr (!B_KN && GEMM_PIPE) {
+        if constexpr (!B_KN) {
             run_nk(p, smem, m0, n0, m_used, kb, klen, tid, acc);
             return;
         }
