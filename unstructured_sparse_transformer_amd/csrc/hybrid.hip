@@ -218,7 +218,13 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define HB_KB 128
 #endif
 #ifndef HB_STAGES
-#define HB_STAGES 4
+#define HB_STAGES 3
+#endif
+#ifndef HB_PER_CU
+#define HB_PER_CU 2
+#endif
+#ifndef DN_PER_CU
+#define DN_PER_CU 1
 #endif
 #ifndef DN_KB
 #define DN_KB 128
@@ -348,20 +354,22 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 
 // Small-M tile shapes for the hybrid GEMMs (M = overflow rows, a few hundred;
 // they stream whole weight matrices, so each workgroup keeps several K stages
-// of copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 4-deep
-// ring of 128-byte K stages; down: 64 x 256, 4 waves, 3-deep ring with the
-// W_d stage transposed in LDS, split over K.
+// of copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 3-deep
+// ring of 128-byte K stages (72 KiB), two workgroups per CU; down: 64 x 256,
+// 4 waves, 3-deep ring with the W_d stage transposed in LDS (152 KiB, one per
+// CU), split over K.
 constexpr int HB_BM = 64, HB_WM = 32;
 constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32, DN_WN = 128;
 
 // Workgroups for a tile loop: one per CU, at most `tiles`, rounded down to a
 // multiple of 8 when that many (keeps N columns on one XCD).
-static int loop_grid(long tiles)
+static int loop_grid(long tiles, int per_cu = 1)
 {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    long g = tiles < ncu ? tiles : ncu;
+    const long slots = (long)ncu * per_cu;
+    long g = tiles < slots ? tiles : slots;
     if (g >= 8)
         g &= ~7L;
     return (int)(g > 0 ? g : 1);
@@ -390,7 +398,7 @@ static hipError_t dense_go(const void *x, int T, const void *w_t, const int32_t 
     p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
     DenseOut<TI> o{static_cast<TI *>(out), static_cast<const TI *>(gate)};
     dense_epi_kernel<TI, HB_BM, HB_BN, HB_WM, HB_WN, MODE>
-        <<<dim3(loop_grid((long)p.MT * p.NT)), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);
+        <<<dim3(loop_grid((long)p.MT * p.NT, HB_PER_CU)), dim3((HB_BM / HB_WM) * (HB_BN / HB_WN) * 64), 0, s>>>(p, o);
     return hipGetLastError();
 }
 
@@ -446,7 +454,7 @@ static hipError_t down_go(const void *pbuf, const void *wd, const int32_t *ovf_r
     p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
     DownOut<TI> o{part, y, ovf_rows, splits};
     down_kernel<TI, DN_BM, DN_BN, DN_WM, DN_WN>
-        <<<dim3(loop_grid((long)p.MT * p.NT * splits)), dim3((DN_BM / DN_WM) * (DN_BN / DN_WN) * 64), 0, s>>>(p, o);
+        <<<dim3(loop_grid((long)p.MT * p.NT * splits, DN_PER_CU)), dim3((DN_BM / DN_WM) * (DN_BN / DN_WN) * 64), 0, s>>>(p, o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;
