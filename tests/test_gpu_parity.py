@@ -178,6 +178,30 @@ def test_max_ovf_zero(gpu_lib):
     assert not out["y"][ref.ovf_local].any()
 
 
+def test_fused_order_out_of_range(gpu_lib):
+    """Order entries outside 0..T-1 are skipped (their workgroups write nothing);
+    the valid ones are served as usual."""
+    import torch
+    import unstructured_sparse_transformer_amd as tw
+    from helpers import to_device
+    wl = make_random_small(64, 128, 512, 128, 8, "bf16", active_frac=0.05, seed=17, jitter=0.5)
+    say("case fused order with out-of-range entries")
+    dt, x, wg, wu, wd = to_device(wl)
+    hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, wl.T)
+    tw.twell_pack_gate_hybrid(x, wg, hy)
+    order = torch.full((wl.T,), -1, dtype=torch.int32, device="cuda")
+    order[::2] = torch.arange(0, wl.T, 2, dtype=torch.int32, device="cuda")
+    order[1] = wl.T + 5
+    y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    yref = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=order)
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, yref)
+    torch.cuda.synchronize()
+    y, yref = y.cpu().numpy(), yref.cpu().numpy()
+    np.testing.assert_array_equal(y[0::2], yref[0::2])
+    assert np.isnan(y[1::2]).all()
+
+
 def test_zero_rows(gpu_lib):
     import torch
     import unstructured_sparse_transformer_amd as tw
