@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    ap.add_argument("--no-energy", action="store_true", help="skip the energy-per-token measurement")
+    ap.add_argument("--energy-seconds", type=float, default=2.0, help="run time per energy measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a plain 256 MiB streaming kernel 3x first (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -268,6 +270,13 @@ def main():
                                  "tflops": round(3 * gate_flop / (dms * 1e-3) / 1e12, 1),
                                  "sparse_speedup": round(dms / ms_per_step, 3)}
 
+    # ---- energy per token, sparse path vs the dense FFN (board energy counter)
+    if not args.no_energy:
+        fns = {"sparse": step}
+        if not args.no_dense:
+            fns["dense"] = dense_step
+        out["energy"] = energy_per_token(fns, wl.T, args.energy_seconds, torch)
+
     # ---- CPU oracle on a bounded sample of the same workload (rank 0, N=1)
     if not args.no_cpu_baseline:
         import oracle
@@ -300,6 +309,46 @@ def main():
                                          f"gate + C TwELL packer, partition, dense backup and fused sum "
                                          f"({dt2:.1f} s)"}
     print(json.dumps(out), flush=True)
+
+
+def energy_per_token(fns, tokens_per_call, seconds, torch):
+    """Joules per token of each callable, from the GPU's cumulative energy
+    counter read before and after about `seconds` of back-to-back calls."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as ex:  # no energy counter on this machine
+        return {"error": f"energy counter unavailable: {ex!r}"}
+
+    def joules():
+        e = amdsmi.amdsmi_get_energy_count(handle)
+        return e["energy_accumulator"] * e["counter_resolution"] * 1e-6
+
+    res = {}
+    try:
+        for name, fn in fns.items():
+            fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            calls = 0
+            while time.perf_counter() - t0 < 0.2:  # size the loop
+                fn()
+                calls += 1
+            torch.cuda.synchronize()
+            n = max(1, int(calls * seconds / max(time.perf_counter() - t0, 1e-3)))
+            j0, t0 = joules(), time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            j1, t1 = joules(), time.perf_counter()
+            res[name] = {"J_per_token": (j1 - j0) / (n * tokens_per_call), "avg_power_W": round((j1 - j0) / (t1 - t0), 1),
+                         "seconds": round(t1 - t0, 2), "calls": n}
+    finally:
+        amdsmi.amdsmi_shut_down()
+    if "sparse" in res and "dense" in res:
+        res["sparse_vs_dense"] = round(res["sparse"]["J_per_token"] / res["dense"]["J_per_token"], 4)
+    return res
 
 
 def run_stack(args, tw, torch, np):
