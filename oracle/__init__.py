@@ -19,12 +19,16 @@ Models", gist.science summary page):
   holds more than ``cap`` actives; backup rows in ascending token order).
 * ``ffn_dense`` / ``ffn_twell`` / ``ffn_active``: section 2.2, y = (ReLU(x.W_g)
   * x.W_u) . W_d, accumulated over neurons in ascending order in fp64.
+* ``gate_stats``: section 2.4's L1 activation penalty and dead neurons, as
+  per-neuron active counts and per (row, tile) sums of the active gate values.
 
 Pins (tests/test_oracle.py): pure-Python brute force on tiny inputs, all 2^8
 patterns of one 8-wide tile, a hand-worked example (tests/golden), closed forms
 (all dead; one active neuron; dense tile; identity up/down), dense == sparse
-bitwise, nonzero conservation, round trip, numpy fp64 matmul cross-check, and
-bf16 rounding against torch's conversion.
+bitwise, nonzero conservation, round trip, numpy fp64 matmul cross-check,
+bf16 rounding against torch's conversion, and for ``gate_stats`` brute force,
+conservation against the TwELL counts and closed forms (all dead, all active,
+one live neuron).
 """
 
 from __future__ import annotations
@@ -58,6 +62,7 @@ def _load():
     lib.orc_partition.argtypes = [P, I, I, I, P, P]
     lib.orc_partition.restype = I
     lib.orc_ffn_dense.argtypes = [P, P, P, I, I, I, I, P]
+    lib.orc_gate_stats.argtypes = [P, I, I, I, P, P]
     lib.orc_ffn_twell.argtypes = [P, P, P, I, I, I, I, P, P, P, I, I, P]
     lib.orc_ffn_active.argtypes = [P, I, I, P, P, P, I, I, P]
     _lib = lib
@@ -141,6 +146,19 @@ def pack_twell(z: np.ndarray, tile_w: int, cap: int, vdtype) -> TwELL:
     idx = np.empty((T, n_b, cap), np.uint8)
     lib.orc_pack_twell(_p(z), T, F, tile_w, cap, _vd(vdtype), _p(cnt), _p(val), _p(idx))
     return TwELL(T, F, tile_w, cap, cnt, val, idx)
+
+
+def gate_stats(z: np.ndarray, tile_w: int):
+    """Activation statistics of the gate (section 2.4's L1 activation penalty
+    and dead neurons): per-neuron count of rows with z > 0 ([F] int64) and per
+    (row, tile) sum of the active z values ([T][n_b] fp64, before rounding)."""
+    lib = _load()
+    z = _c(z, np.float64)
+    T, F = z.shape
+    cnt = np.zeros(F, dtype=np.int64)
+    l1 = np.zeros((T, F // tile_w), dtype=np.float64)
+    lib.orc_gate_stats(_p(z), T, F, tile_w, _p(cnt), _p(l1))
+    return cnt, l1
 
 
 def unpack_twell(tw: TwELL) -> np.ndarray:

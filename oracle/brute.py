@@ -76,3 +76,17 @@ def ffn(x, wg_t, wu_t, wd, hround=None):
                     acc[k] += (h * u) * wd[j][k]
         y.append(acc)
     return y
+
+
+def gate_stats(z, w: int):
+    """Per-neuron active counts and per (row, tile) sums of active values
+    (section 2.4's L1 activation penalty), by nested loops over lists."""
+    T, F = len(z), len(z[0])
+    cnt = [0] * F
+    l1 = [[0.0] * (F // w) for _ in range(T)]
+    for t in range(T):
+        for j in range(F):
+            if z[t][j] > 0.0:
+                cnt[j] += 1
+                l1[t][j // w] += z[t][j]
+    return cnt, l1

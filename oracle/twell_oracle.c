@@ -231,3 +231,28 @@ EXPORT void orc_ffn_active(const double *z, int T, int F,
         }
     }
 }
+
+/* Activation statistics of the gate (the page's L1 activation penalty, section
+ * 2.4, and its dead neurons): neuron_cnt[j] = number of rows t with z[t][j] > 0;
+ * l1[t][b] = sum over the active columns j of tile b of row t of z[t][j]
+ * (the gate activation before rounding; ascending columns, fp64). */
+EXPORT void orc_gate_stats(const double *z, int T, int F, int w, int64_t *neuron_cnt, double *l1)
+{
+    const int n_b = F / w;
+    for (int j = 0; j < F; ++j)
+        neuron_cnt[j] = 0;
+    for (int t = 0; t < T; ++t) {
+        for (int b = 0; b < n_b; ++b) {
+            double s = 0.0;
+            for (int c = 0; c < w; ++c) {
+                const int j = b * w + c;
+                const double zz = z[(int64_t)t * F + j];
+                if (zz > 0.0) {
+                    s += zz;
+                    neuron_cnt[j] += 1;
+                }
+            }
+            l1[(int64_t)t * n_b + b] = s;
+        }
+    }
+}

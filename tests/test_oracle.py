@@ -237,3 +237,49 @@ def test_nan_and_signed_zero_inactive(w, cap):
     tw = oracle.pack_twell(z, w, cap, "f32")
     assert tw.cnt[:, 0].tolist() == [0, 1, 1]
     assert tw.idx[1, 0, 0] == 5 and tw.idx[2, 0, 0] == w - 1
+
+
+# ------------------------------------------------------------ gate activation statistics
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("w", [4, 8, 32])
+def test_gate_stats_against_brute_force(seed, w):
+    rng = np.random.default_rng(2000 + seed)
+    T = int(rng.integers(1, 7))
+    F = w * int(rng.integers(1, 5))
+    z = rng.integers(-6, 7, (T, F)) / 4.0
+    cnt, l1 = oracle.gate_stats(z, w)
+    cb, lb = brute.gate_stats(z.tolist(), w)
+    assert list(cnt) == cb
+    np.testing.assert_array_equal(l1, np.asarray(lb))
+
+
+@pytest.mark.parametrize("w,cap", [(32, 4), (64, 8), (256, 16)])
+def test_gate_stats_against_twell(w, cap):
+    """Counts conserve the TwELL true counts; with cap = tile width and exact
+    storage every active value is stored, so each tile's stored values sum to l1."""
+    wl = make_random_small(T=48, d=64, F=512, tile_w=w, cap=cap, active_frac=0.1, seed=11, jitter=0.5)
+    z = oracle.gate(wl.x, wl.wg_t)
+    cnt, l1 = oracle.gate_stats(z, w)
+    tw = oracle.pack_twell(z, w, cap, "bf16")
+    assert cnt.sum() == tw.cnt.sum()
+    full = oracle.pack_twell(z, w, w, "exact")
+    np.testing.assert_array_equal(cnt, (oracle.unpack_twell(full) > 0).sum(0))
+    np.testing.assert_allclose(l1, full.val.sum(2), rtol=1e-14, atol=0)
+    assert (l1 >= 0).all() and ((l1 > 0) == (tw.cnt > 0)).all()
+
+
+def test_gate_stats_closed_forms():
+    T, F, w = 5, 64, 16
+    cnt, l1 = oracle.gate_stats(np.full((T, F), -1.0), w)
+    assert not cnt.any() and not l1.any()
+    cnt, l1 = oracle.gate_stats(np.full((T, F), 0.5), w)
+    assert (cnt == T).all() and (l1 == 0.5 * w).all()
+    z = np.full((T, F), -2.0)
+    z[:, 7] = np.arange(1, T + 1)  # one live neuron, the rest dead
+    z[0, 9] = np.nan
+    z[1, 9] = -0.0
+    z[2, 9] = 0.0
+    cnt, l1 = oracle.gate_stats(z, w)
+    assert cnt[7] == T and cnt.sum() == T
+    np.testing.assert_array_equal(l1[:, 0], np.arange(1, T + 1))
+    assert not l1[:, 1:].any()
