@@ -107,6 +107,23 @@ typedef struct twell_hybrid_t {
  * Returns TWELL_OK or a negative twell_status. */
 TWELL_API int twell_pack_gate(const void *x, const void *wg_t, int32_t d, const twell_t *h, void *stream);
 
+/* twell_pack_gate plus activation statistics taken in the same epilogue
+ * (section 2.4 of the page: the L1 penalty on the activations that training
+ * adds, and the neurons it leaves dead).  Writes the same TwELL, and:
+ *   neuron_cnt : device [h->F] int32, ADDED TO with atomics: per neuron j,
+ *                the number of rows t with (x . W_g)[t][j] > 0.  Zero it
+ *                before the first call; calls accumulate, so a neuron still at
+ *                0 after a set of calls is dead on all their rows.  The caller
+ *                keeps the accumulated rows under 2^31.
+ *   l1         : device [h->T][h->F / h->tile_w] float, overwritten: per
+ *                (row, tile), the sum of the positive gate values of the tile
+ *                (fp32 accumulators, before rounding to vdtype), added in a
+ *                fixed order, so repeated calls give the same bits.  The L1
+ *                term of a row is the sum of its tiles.
+ * Both 4-byte aligned.  Returns TWELL_OK or a negative twell_status. */
+TWELL_API int twell_pack_gate_stats(const void *x, const void *wg_t, int32_t d, const twell_t *h,
+                                    int32_t *neuron_cnt, float *l1, void *stream);
+
 /* Overflow partition and dense backup (section 2.3 of the page): from
  * hy->ell.cnt (written by twell_pack_gate) computes row_ovf, the ascending
  * ovf_rows list and n_ovf, then recomputes ReLU(x . W_g) for the first

@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 100
+    assert lib.twell_version() == 101
 
 
 def test_status_strings():
@@ -38,6 +38,21 @@ def _desc(T=16, F=512, w=128, cap=8, vd=1, val=256, idx=512, cnt=1024):
 
 
 GOOD = 4096  # an aligned, never dereferenced fake device address
+
+
+def test_pack_gate_stats_validation():
+    lib = tw.load()
+    f = lib.twell_pack_gate_stats
+    d = ctypes.byref(_desc())
+    assert f(GOOD, GOOD, 64, None, GOOD, GOOD, None) == -1
+    assert f(GOOD, GOOD, 64, d, None, GOOD, None) == -1                     # neuron_cnt NULL
+    assert f(GOOD, GOOD, 64, d, GOOD, None, None) == -1                     # l1 NULL
+    assert f(GOOD, GOOD, 64, d, GOOD + 2, GOOD, None) == -2                 # neuron_cnt misaligned
+    assert f(GOOD, GOOD, 64, d, GOOD, GOOD + 1, None) == -2                 # l1 misaligned
+    assert f(None, GOOD, 64, d, GOOD, GOOD, None) == -1                     # x NULL
+    assert f(GOOD, GOOD, 65, d, GOOD, GOOD, None) == -3                     # d % 64
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(w=100)), GOOD, GOOD, None) == -4
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(T=0)), GOOD, GOOD, None) == 0  # nothing to do
 
 
 def test_pack_gate_validation():

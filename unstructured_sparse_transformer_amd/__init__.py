@@ -6,7 +6,7 @@ memory and the current HIP stream.  There is no CPU fallback: ``load()``
 raises when the library is missing, and every call raises on a non-OK status.
 
 The functions carry the C names (``include/twell.h``):
-``twell_pack_gate``, ``twell_partition_overflow``, ``twell_pack_gate_hybrid``,
+``twell_pack_gate``, ``twell_pack_gate_stats``, ``twell_partition_overflow``, ``twell_pack_gate_hybrid``,
 ``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
 ``twell_ffn_hybrid_workspace_bytes``.
 """
@@ -23,8 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libtwell.so")
 TWELL_F32, TWELL_BF16 = 0, 1
 STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_SHAPE",
           -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE"}
-EXPORTS = ("twell_pack_gate", "twell_partition_overflow", "twell_pack_gate_hybrid", "twell_ffn_fused",
-           "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid", "twell_status_str",
+EXPORTS = ("twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
+           "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid", "twell_status_str",
            "twell_version")
 
 
@@ -61,6 +61,7 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     P, I32 = ctypes.c_void_p, ctypes.c_int32
     lib.twell_pack_gate.argtypes = [P, P, I32, ctypes.POINTER(TwellT), P]
+    lib.twell_pack_gate_stats.argtypes = [P, P, I32, ctypes.POINTER(TwellT), P, P, P]
     lib.twell_partition_overflow.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
     lib.twell_pack_gate_hybrid.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
     lib.twell_ffn_fused.argtypes = [ctypes.POINTER(TwellT), P, P, P, P, I32, P, P]
@@ -71,7 +72,7 @@ def load(path: str = LIB_PATH):
     lib.twell_status_str.argtypes = [ctypes.c_int]
     lib.twell_status_str.restype = ctypes.c_char_p
     lib.twell_version.restype = ctypes.c_int
-    for fn in (lib.twell_pack_gate, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
+    for fn in (lib.twell_pack_gate, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
                lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow):
         fn.restype = ctypes.c_int
     _lib = lib
@@ -165,6 +166,14 @@ def twell_pack_gate(x, wg_t, tw: TwELL, stream=None):
     lib = load()
     d = ctypes.byref(tw.desc())
     _check("twell_pack_gate", lib.twell_pack_gate(_ptr(x), _ptr(wg_t), int(x.shape[1]), d, _stream(stream)))
+
+
+def twell_pack_gate_stats(x, wg_t, tw: TwELL, neuron_cnt, l1, stream=None):
+    """neuron_cnt: int32 [F] (added to); l1: float32 [T][F // tile_w] (overwritten)."""
+    lib = load()
+    d = ctypes.byref(tw.desc())
+    _check("twell_pack_gate_stats", lib.twell_pack_gate_stats(_ptr(x), _ptr(wg_t), int(x.shape[1]), d,
+                                                              _ptr(neuron_cnt), _ptr(l1), _stream(stream)))
 
 
 def twell_partition_overflow(x, wg_t, hy: Hybrid, stream=None):

@@ -97,7 +97,7 @@ size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
 
 extern "C" {
 
-int twell_version(void) { return 100; }
+int twell_version(void) { return 101; }
 
 const char *twell_status_str(int status)
 {
@@ -131,6 +131,24 @@ int twell_pack_gate(const void *x, const void *wg_t, int32_t d, const twell_t *h
     TWELL_TRY(check_ptrs(h));
     return hip_status(twell::launch_gate_twell(h->vdtype, x, wg_t, h->T, d, h->F, h->tile_w, h->cap, h->val, h->idx,
                                                h->cnt, static_cast<hipStream_t>(stream)));
+}
+
+int twell_pack_gate_stats(const void *x, const void *wg_t, int32_t d, const twell_t *h, int32_t *neuron_cnt,
+                          float *l1, void *stream)
+{
+    TWELL_TRY(check_layout(h, d));
+    if (!neuron_cnt || !l1)
+        return TWELL_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(neuron_cnt) | reinterpret_cast<uintptr_t>(l1)) & 3u)
+        return TWELL_E_ALIGN;
+    if (h->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wg_t));
+    TWELL_TRY(check_ptrs(h));
+    return hip_status(twell::launch_gate_twell_stats(h->vdtype, x, wg_t, h->T, d, h->F, h->tile_w, h->cap, h->val,
+                                                     h->idx, h->cnt, neuron_cnt, l1,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 int twell_partition_overflow(const void *x, const void *wg_t, int32_t d, const twell_hybrid_t *hy, void *stream)

@@ -452,9 +452,177 @@ __device__ __forceinline__ void twell_epilogue_seg(f32x16 (&acc)[WM / 32][WN / 3
     }
 }
 
-template <typename TI, int BM, int BN, int WM, int WN, int TW, int KB, int STAGES, int WPE>
+// Activation statistics of the gate (section 2.4 of the page: the L1
+// penalty on the activations that training adds, and the neurons it leaves
+// dead), gathered from the same accumulators before the packing.
+struct GateStats {
+    int32_t *neuron_cnt;  // [N]: rows with z > 0 per neuron, added atomically
+    float *l1;            // [M][n_b]: sum of the positive z of each (row, tile)
+};
+
+// v from the lane whose index differs in bit log2(MASK) (inside 32 lanes):
+// DPP for 1, 2 (quad permutes) and 8 (row rotate by 8), ds_swizzle's xor
+// mode for 4 and 16.
+template <int MASK> __device__ __forceinline__ float lane_xor(float v)
+{
+    const int b = __float_as_int(v);
+    int r;
+    if constexpr (MASK == 1)
+        r = __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false);
+    else if constexpr (MASK == 2)
+        r = __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false);
+    else if constexpr (MASK == 8)
+        r = __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false);
+    else
+        r = __builtin_amdgcn_ds_swizzle(b, 0x1F | (MASK << 10));
+    return __int_as_float(r);
+}
+
+// One halving step of a transposing reduction: lanes with bit BIT clear keep
+// registers [0, N) and lanes with it set keep [N, 2N); each adds its partner's
+// copy of the registers it keeps.
+// (The lane test is a constant lane mask in SGPRs, not a per-lane value:
+// per-lane lane bits would be long-lived VGPRs.)
+template <int BIT> __device__ __forceinline__ float lane_bit_select(float if_clear, float if_set)
+{
+    constexpr uint64_t m = BIT == 4   ? 0xFFFF0000FFFF0000ull
+                           : BIT == 3 ? 0xFF00FF00FF00FF00ull
+                           : BIT == 2 ? 0xF0F0F0F0F0F0F0F0ull
+                                      : 0xCCCCCCCCCCCCCCCCull;
+    static_assert(BIT >= 1 && BIT <= 4, "lane bit");
+    float r;
+    asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(m));
+    return r;
+}
+
+template <int BIT, int N> __device__ __forceinline__ void fold_half(float (&v)[16])
+{
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const float send = lane_bit_select<BIT>(v[k + N], v[k]);
+        const float keep = lane_bit_select<BIT>(v[k], v[k + N]);
+        v[k] = keep + lane_xor<1 << BIT>(send);
+    }
+}
+
+// Sums each of 16 registers over the 32 lanes of a half-wave in 16 exchanges
+// (not 16 x 5): lane p of the half returns the sum of register p >> 1.  The
+// tree is fixed, so the result does not depend on timing.
+__device__ __forceinline__ float half_wave_sum16(float (&v)[16])
+{
+    fold_half<4, 8>(v);
+    fold_half<3, 4>(v);
+    fold_half<2, 2>(v);
+    fold_half<1, 1>(v);
+    return v[0] + lane_xor<1>(v[0]);
+}
+
+// Activation statistics from the accumulators of one BM x BN output tile,
+// taken before the packing (rows < M only):
+//  * per (row, TwELL tile), the sum of the positive z: per lane, the positive
+//    values of a group of min(TW, WN) columns are added in ascending block
+//    order, the 32 lanes of each half-wave are reduced with half_wave_sum16,
+//    and a tile wider than a wave adds its two waves' groups in column order;
+//  * per column, the rows with z > 0: per lane over its rows, then the
+//    2 x (BM / WM) lanes that share a column are added in LDS and go out with
+//    one atomic add.
+// The activity test is integer arithmetic on max(z, 0) in inline assembly,
+// not a compare: the compiler turns any visible form of it back into a
+// compare, merges that with the packing's ballots and keeps the masks live
+// across both, spilling registers.  Uses the first BM * BN / 8 + (BM / WM) * BN * 8 bytes of smem;
+// ends with a barrier.
+template <int BM, int BN, int WM, int WN, int TW, int LDS_BYTES, bool PARTIAL>
+__device__ __forceinline__ void gate_stats_tile(const f32x16 (&acc)[WM / 32][WN / 32], char *smem, int m0, int n0,
+                                                int M, int N, int n_b, const GateStats &st)
+{
+    constexpr int FM = WM / 32, FN = WN / 32, NWN = BN / WN, NWM = BM / WM;
+    constexpr int NTHR = NWM * NWN * 64;
+    constexpr int GW = TW < WN ? TW : WN;  // columns of one row-sum group
+    constexpr int GPW = WN / GW;           // groups per wave
+    constexpr int FPG = GW / 32;           // accumulator blocks per group
+    constexpr int GPR = BN / GW;           // groups per workgroup row
+    constexpr int GPT = TW / GW;           // groups per TwELL tile (1 or 2)
+    constexpr int TPW = BN / TW;           // TwELL tiles per workgroup row
+    static_assert(GPT == 1 || GPT == 2, "a TwELL tile spans at most two waves");
+    float *spart = reinterpret_cast<float *>(smem);                    // [BM][GPR]
+    int32_t *scol = reinterpret_cast<int32_t *>(smem + BM * GPR * 4);  // [2 * NWM][BN]
+    static_assert(BM * GPR * 4 + 2 * NWM * BN * 4 <= LDS_BYTES, "statistics LDS");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int rows_left = M - (m0 + wm * WM);  // rows of this wave below M
+
+    int ccnt[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        ccnt[fn] = 0;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = 0.f;
+#pragma unroll
+                for (int f = 0; f < FPG; ++f) {
+                    // r = max(z, 0) (the accumulators hold no signalling NaN, and a
+                    // quiet NaN gives 0); the count grows by 1 iff r is not +-0,
+                    // i.e. z > 0 (and, PARTIAL, the row is below M).  The count is
+                    // an in-out operand so each add happens here: deferred adds
+                    // would keep every activity bit live.
+                    float r;
+                    uint32_t t;
+                    if constexpr (PARTIAL) {
+                        const uint32_t live = (uint32_t)(fm * 32 + acc_row(i, lane) - rows_left) >> 31;
+                        asm("v_max_f32 %0, 0, %3\n\tv_lshlrev_b32 %1, 1, %0\n\tv_min_u32 %1, 1, %1\n\t"
+                            "v_and_b32 %1, %1, %4\n\tv_add_u32 %2, %2, %1"
+                            : "=&v"(r), "=&v"(t), "+v"(ccnt[g * FPG + f])
+                            : "v"(acc[fm][g * FPG + f][i]), "v"(live));
+                    } else {
+                        asm("v_max_f32 %0, 0, %3\n\tv_lshlrev_b32 %1, 1, %0\n\tv_min_u32 %1, 1, %1\n\t"
+                            "v_add_u32 %2, %2, %1"
+                            : "=&v"(r), "=&v"(t), "+v"(ccnt[g * FPG + f])
+                            : "v"(acc[fm][g * FPG + f][i]));
+                    }
+                    s += r;
+                }
+                v[i] = s;
+            }
+            const float r = half_wave_sum16(v);
+            if (!(lane & 1)) {
+                const int row = wm * WM + fm * 32 + acc_row((lane & 31) >> 1, lane);
+                spart[row * GPR + wn * GPW + g] = r;
+            }
+        }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        scol[(wm * 2 + (lane >> 5)) * BN + wn * WN + fn * 32 + (lane & 31)] = ccnt[fn];
+    __syncthreads();
+
+    for (int e = tid; e < BM * TPW; e += NTHR) {
+        const int r = e / TPW, tl = e - r * TPW;
+        float s = spart[r * GPR + tl * GPT];
+        if constexpr (GPT == 2)
+            s += spart[r * GPR + tl * GPT + 1];
+        const int t = m0 + r, gcol = n0 + tl * TW;
+        if (t < M && gcol < N)
+            st.l1[(int64_t)t * n_b + gcol / TW] = s;
+    }
+    for (int c = tid; c < BN; c += NTHR) {
+        int s = 0;
+#pragma unroll
+        for (int j = 0; j < 2 * NWM; ++j)
+            s += scol[j * BN + c];
+        if (s && n0 + c < N)
+            atomicAdd(st.neuron_cnt + n0 + c, s);
+    }
+    __syncthreads();
+}
+
+template <typename TI, int BM, int BN, int WM, int WN, int TW, int KB, int STAGES, int WPE, bool STATS>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
-gate_twell_kernel(GemmArgs p, TwellOut<TI> o)
+gate_twell_kernel(GemmArgs p, TwellOut<TI> o, GateStats st)
 {
     using Core = GemmCore<TI, BM, BN, WM, WN, false, KB, STAGES>;
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
@@ -464,15 +632,21 @@ gate_twell_kernel(GemmArgs p, TwellOut<TI> o)
     Core core;
     f32x16 acc[Core::FM][Core::FN];
     core.run(p, smem, m0, n0, p.M, p.k_begin, p.k_len, threadIdx.x, acc);
+    if constexpr (STATS) {
+        if (m0 + BM <= p.M)
+            gate_stats_tile<BM, BN, WM, WN, TW, Core::LDS_BYTES, false>(acc, smem, m0, n0, p.M, p.N, o.n_b, st);
+        else
+            gate_stats_tile<BM, BN, WM, WN, TW, Core::LDS_BYTES, true>(acc, smem, m0, n0, p.M, p.N, o.n_b, st);
+    }
     if (seg_fits<TI, BM, BN, WN, TW, Core::LDS_BYTES>(o.cap))
         twell_epilogue_seg<TI, BM, BN, WM, WN, TW, Core::LDS_BYTES>(acc, smem, m0, n0, p.M, p.N, o);
     else
         twell_epilogue<TI, BM, BN, WM, WN, TW, Core::LDS_BYTES>(acc, smem, m0, n0, p.M, p.N, o);
 }
 
-template <typename TI, int BM, int BN, int WM, int WN, int KB, int STAGES, int WPE>
+template <typename TI, int BM, int BN, int WM, int WN, int KB, int STAGES, int WPE, bool STATS>
 static hipError_t gate_twell_go(const void *x, const void *wg_t, int T, int d, int F, int tile_w, int cap, void *val,
-                                uint8_t *idx, int32_t *cnt, hipStream_t s)
+                                uint8_t *idx, int32_t *cnt, const GateStats &st, hipStream_t s)
 {
     GemmArgs p{};
     p.A = x;
@@ -492,30 +666,46 @@ static hipError_t gate_twell_go(const void *x, const void *wg_t, int T, int d, i
     const dim3 grid(p.MT * p.NT), block(NTHR);
     switch (tile_w) {
     case 32:
-        gate_twell_kernel<TI, BM, BN, WM, WN, 32, KB, STAGES, WPE><<<grid, block, 0, s>>>(p, o);
+        gate_twell_kernel<TI, BM, BN, WM, WN, 32, KB, STAGES, WPE, STATS><<<grid, block, 0, s>>>(p, o, st);
         break;
     case 64:
-        gate_twell_kernel<TI, BM, BN, WM, WN, 64, KB, STAGES, WPE><<<grid, block, 0, s>>>(p, o);
+        gate_twell_kernel<TI, BM, BN, WM, WN, 64, KB, STAGES, WPE, STATS><<<grid, block, 0, s>>>(p, o, st);
         break;
     case 128:
-        gate_twell_kernel<TI, BM, BN, WM, WN, 128, KB, STAGES, WPE><<<grid, block, 0, s>>>(p, o);
+        gate_twell_kernel<TI, BM, BN, WM, WN, 128, KB, STAGES, WPE, STATS><<<grid, block, 0, s>>>(p, o, st);
         break;
     default:
-        gate_twell_kernel<TI, BM, BN, WM, WN, 256, KB, STAGES, WPE><<<grid, block, 0, s>>>(p, o);
+        gate_twell_kernel<TI, BM, BN, WM, WN, 256, KB, STAGES, WPE, STATS><<<grid, block, 0, s>>>(p, o, st);
         break;
     }
     return hipGetLastError();
 }
 
 // Tile shapes: bf16 as configured above, fp32 64 x 256 (4 waves of 32 x 128).
+template <bool STATS>
+static hipError_t gate_twell_dispatch(int vdtype, const void *x, const void *wg_t, int T, int d, int F, int tile_w,
+                                      int cap, void *val, uint8_t *idx, int32_t *cnt, const GateStats &st,
+                                      hipStream_t s)
+{
+    if (vdtype == 1)
+        return gate_twell_go<__bf16, GATE_BM, 256, GATE_WM, 128, GATE_KB, GATE_STAGES, GATE_WPE, STATS>(
+            x, wg_t, T, d, F, tile_w, cap, val, idx, cnt, st, s);
+    return gate_twell_go<float, 64, 256, 32, 128, 128, 2, 1, STATS>(x, wg_t, T, d, F, tile_w, cap, val, idx, cnt, st,
+                                                                    s);
+}
+
 hipError_t launch_gate_twell(int vdtype, const void *x, const void *wg_t, int T, int d, int F, int tile_w, int cap,
                              void *val, uint8_t *idx, int32_t *cnt, hipStream_t s)
 {
-    if (vdtype == 1)
-        return gate_twell_go<__bf16, GATE_BM, 256, GATE_WM, 128, GATE_KB, GATE_STAGES, GATE_WPE>(x, wg_t, T, d, F,
-                                                                                               tile_w, cap, val,
-                                                                              idx, cnt, s);
-    return gate_twell_go<float, 64, 256, 32, 128, 128, 2, 1>(x, wg_t, T, d, F, tile_w, cap, val, idx, cnt, s);
+    return gate_twell_dispatch<false>(vdtype, x, wg_t, T, d, F, tile_w, cap, val, idx, cnt, GateStats{}, s);
+}
+
+hipError_t launch_gate_twell_stats(int vdtype, const void *x, const void *wg_t, int T, int d, int F, int tile_w,
+                                   int cap, void *val, uint8_t *idx, int32_t *cnt, int32_t *neuron_cnt, float *l1,
+                                   hipStream_t s)
+{
+    return gate_twell_dispatch<true>(vdtype, x, wg_t, T, d, F, tile_w, cap, val, idx, cnt,
+                                     GateStats{neuron_cnt, l1}, s);
 }
 
 }  // namespace twell

@@ -11,6 +11,12 @@ namespace twell {
 hipError_t launch_gate_twell(int vdtype, const void *x, const void *wg_t, int T, int d, int F, int tile_w,
                              int cap, void *val, uint8_t *idx, int32_t *cnt, hipStream_t s);
 
+// The same, plus per-neuron active-row counts (added to neuron_cnt [F]) and
+// per (row, tile) sums of the positive gate values (l1 [T][F / tile_w]).
+hipError_t launch_gate_twell_stats(int vdtype, const void *x, const void *wg_t, int T, int d, int F, int tile_w,
+                                   int cap, void *val, uint8_t *idx, int32_t *cnt, int32_t *neuron_cnt, float *l1,
+                                   hipStream_t s);
+
 // row_ovf[t] = any tile of row t has cnt > cap; work[t] = stored entries of
 // row t (0 for an overflow row).
 hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, int32_t *work,
