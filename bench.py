@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-energy", action="store_true", help="skip the energy-per-token measurement")
+    ap.add_argument("--no-stats", action="store_true", help="skip the gate-statistics variant timing")
     ap.add_argument("--energy-seconds", type=float, default=2.0, help="run time per energy measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a plain 256 MiB streaming kernel 3x first (counter calibration under rocprofv3)")
@@ -231,6 +232,28 @@ def main():
         "memory": {"twell_bytes": int(wl.T * n_b * (4 + wl.cap * (esz + 1))),
                    "dense_backup_bytes": int(n_ovf * wl.F * esz), "dense_h_bytes": int(wl.T * wl.F * esz)},
     }
+
+    # ---- gate with the activation statistics (per-neuron active counts, per-tile
+    # L1 sums) against the plain gate, alternating, after the timed region
+    if not args.no_stats:
+        ncnt = torch.zeros(wl.F, dtype=torch.int32, device=dev)
+        l1 = torch.empty((wl.T, n_b), dtype=torch.float32, device=dev)
+        plain, with_stats = [], []
+        for k in range(args.steps):
+            for fn, acc in ((lambda: tw.twell_pack_gate(x, wg, hy.ell), plain),
+                            (lambda: tw.twell_pack_gate_stats(x, wg, hy.ell, ncnt, l1), with_stats)):
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev[0].record()
+                fn()
+                ev[1].record()
+                acc.append(ev)
+        torch.cuda.synchronize()
+        p_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in plain]))
+        s_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in with_stats]))
+        out["gate_stats"] = {"kernel": "gate_twell_kernel with statistics", "pack_gate_ms": round(p_ms, 4),
+                             "pack_gate_stats_ms": round(s_ms, 4), "overhead_frac": round(s_ms / p_ms - 1, 4),
+                             "dead_neurons": int((ncnt == 0).sum().item()),
+                             "mean_l1_per_token": round(float(l1.sum(1).mean().item()), 4)}
 
     # ---- cold-cache variant: flush MALL/L2 with a 1 GiB write between steps (outside the events)
     if not args.no_cold:
