@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-seconds", type=float, default=0.5,
+                    help="untimed steps before the warmup steps, so the GPU clocks leave their idle state")
     ap.add_argument("--workload", default="layer_2b")
     ap.add_argument("--max-ovf", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -53,6 +55,62 @@ def parse():
 COUNTERS = os.path.join(ROOT, "profiles", "counters_layer_2b.json")
 GATE_SOURCES = ["unstructured_sparse_transformer_amd/csrc/gate_twell.hip",
                 "unstructured_sparse_transformer_amd/csrc/twell_device.h"]
+
+
+class DevEvent:
+    """A timing event on the current HIP stream, recorded with a device-scope
+    release (hipEventReleaseToDevice).  torch.cuda.Event uses the default
+    system-scope release, whose cache write-back adds about 10-20 us to a
+    bracketed kernel on MI355X; with a device-scope release the bracket reads
+    within a few microseconds of the kernel's own duration in a kernel trace.
+    Same interface as torch.cuda.Event: record(), elapsed_time(end) in ms."""
+    _hip = None
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self):
+        import ctypes
+        import torch
+        if DevEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")  # the HIP runtime torch has loaded
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            DevEvent._hip = hip
+        self._ct = ctypes
+        self._torch = torch
+        self.ev = ctypes.c_void_p()
+        st = DevEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), self.RELEASE_TO_DEVICE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self):
+        st = DevEvent._hip.hipEventRecord(self.ev, self._torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end) -> float:
+        f = self._ct.c_float()
+        st = DevEvent._hip.hipEventElapsedTime(self._ct.byref(f), self.ev, end.ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return float(f.value)
+
+    def __del__(self):
+        hip = type(self)._hip
+        if hip is not None and self.ev:
+            hip.hipEventDestroy(self.ev)
+
+
+def settle(step, seconds, torch):
+    """Run untimed steps for about `seconds` (in batches of 20, synchronised):
+    an idle MI355X starts a burst at low clocks, and a handful of warmup steps
+    (a few milliseconds) ends before the clocks have ramped up."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
 
 
 def source_digest(paths):
@@ -151,8 +209,9 @@ def main():
         tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=hy.order)
         tw.twell_ffn_overflow(hy, x, wu, wd, y, ws)
 
-    for _ in range(args.warmup):
-        step()
+    # one step for the workload's statistics (host reads), then the settle and
+    # warmup steps right before the timed region, with no idle gap between
+    step()
     torch.cuda.synchronize()
     n_ovf = int(hy.n_ovf.item())
     if n_ovf > max_ovf:
@@ -166,7 +225,10 @@ def main():
     # ---- timed region: K whole steps back to back.  Only the dominant kernel is
     # bracketed by events (every event record costs a few microseconds of idle
     # GPU between kernels); the per-stage breakdown comes from a separate pass.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[DevEvent() for _ in range(2)] for _ in range(args.steps)]
+    settle(step, args.settle_seconds, torch)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -178,7 +240,7 @@ def main():
     value = wl.T * args.steps / wall
 
     # ---- per-stage breakdown (after the timed region; events between all stages)
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    sev = [[DevEvent() for _ in range(5)] for _ in range(args.steps)]
     for k in range(args.steps):
         step(sev[k])
     torch.cuda.synchronize()
@@ -217,7 +279,8 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "settle_s": args.settle_seconds, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded grid-mode inputs of the workload's shape and sparsity; no trained weights)",
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
@@ -242,7 +305,7 @@ def main():
         for k in range(args.steps):
             for fn, acc in ((lambda: tw.twell_pack_gate(x, wg, hy.ell), plain),
                             (lambda: tw.twell_pack_gate_stats(x, wg, hy.ell, ncnt, l1), with_stats)):
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev = [DevEvent() for _ in range(2)]
                 ev[0].record()
                 fn()
                 ev[1].record()
@@ -261,7 +324,7 @@ def main():
         cold = []
         for k in range(min(args.steps, 10)):
             flush.fill_(float(k))
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev = [DevEvent() for _ in range(5)]
             step(ev)
             torch.cuda.synchronize()
             cold.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
@@ -282,7 +345,7 @@ def main():
         for _ in range(3):
             dense_step()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = DevEvent(), DevEvent()
         e0.record()
         for _ in range(args.steps):
             dense_step()
@@ -401,13 +464,15 @@ def run_stack(args, tw, torch, np):
             tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=hy.order)
             tw.twell_ffn_overflow(hy, x, wu, wd, y, ws)
 
+        if layer == 0:  # later layers follow without idle gaps
+            settle(step, args.settle_seconds, torch)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
         n = int(hy.n_ovf.item())
         if n > max_ovf:
             raise SystemExit(f"layer {layer}: n_ovf={n} exceeds max_ovf={max_ovf}")
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        evs = [[DevEvent() for _ in range(2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
@@ -423,7 +488,7 @@ def run_stack(args, tw, torch, np):
             for _ in range(3):
                 dense_step()
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = DevEvent(), DevEvent()
             e0.record()
             for _ in range(args.steps):
                 dense_step()
