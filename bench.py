@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-energy", action="store_true", help="skip the energy-per-token measurement")
     ap.add_argument("--no-stats", action="store_true", help="skip the gate-statistics variant timing")
+    ap.add_argument("--batch-path", action="store_true",
+                    help="decode-shaped workloads (T <= 64): time the batch path instead of twell_ffn_decode")
     ap.add_argument("--energy-seconds", type=float, default=2.0, help="run time per energy measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a plain 256 MiB streaming kernel 3x first (counter calibration under rocprofv3)")
@@ -163,6 +165,9 @@ def main():
 
     t0 = time.time()
     wl = make_workload(args.workload)
+    if wl.T <= 64 and wl.dtype == "bf16" and not args.batch_path:
+        run_decode(args, wl, tw, torch, np)
+        return
     log(f"workload {wl.name}: T={wl.T} d={wl.d} F={wl.F} {wl.dtype} w={wl.tile_w} cap={wl.cap} "
         f"(generated in {time.time() - t0:.1f}s)")
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -435,6 +440,79 @@ def energy_per_token(fns, tokens_per_call, seconds, torch):
     if "sparse" in res and "dense" in res:
         res["sparse_vs_dense"] = round(res["sparse"]["J_per_token"] / res["dense"]["J_per_token"], 4)
     return res
+
+
+def run_decode(args, wl, tw, torch, np):
+    """Decode-shaped calls (T <= 64, bf16): one twell_ffn_decode call per step
+    (gate, packing and partition, chunked gather, reduction: 4 kernels), next
+    to the batch path's four calls and the dense bf16 FFN on the same rows.
+    Roofline: the step is bound by HBM; its algorithmic bytes are W_g read
+    once, the W_u / W_d rows of every active (row, neuron), x, y and the TwELL
+    written."""
+    dev = "cuda"
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)  # noqa: E731
+    x, wg, wu, wd = to(wl.x), to(wl.wg_t), to(wl.wu_t), to(wl.wd)
+    hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, torch.bfloat16, wl.T)
+    ws = tw.decode_workspace(wl.T, wl.F, wl.d, wl.tile_w)
+    y = torch.empty((wl.T, wl.d), dtype=torch.float32, device=dev)
+
+    def step():
+        tw.twell_ffn_decode(x, wg, wu, wd, hy, y, ws)
+
+    def timed(fn, k):
+        evs = [(DevEvent(), DevEvent()) for _ in range(k)]
+        settle(fn, args.settle_seconds, torch)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in evs:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall * 1e3 / k, float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    ms_wall, ms_ev = timed(step, args.steps)
+    n_ovf = int(hy.n_ovf.item())
+    nnz = int(hy.ell.cnt.sum().item())
+    esz = 2
+    n_b = wl.F // wl.tile_w
+    alg = (wl.F * wl.d * esz + wl.T * wl.d * esz + nnz * 2 * wl.d * esz + wl.T * wl.d * 4 +
+           wl.T * n_b * (4 + wl.cap * (esz + 1)))
+    # the batch path on the same rows
+    hb = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, torch.bfloat16, wl.T)
+    wsb = tw.hybrid_workspace(wl.T, wl.F, wl.d, torch.bfloat16)
+
+    def batch():
+        tw.twell_pack_gate_hybrid(x, wg, hb)
+        tw.twell_ffn_hybrid(hb, x, wu, wd, y, wsb)
+
+    _, ms_batch = timed(batch, args.steps)
+    out = {
+        "metric": METRIC, "value": round(wl.T / (ms_wall * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle_seconds,
+        "ms_per_step": round(ms_wall, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded grid-mode inputs of the workload's shape and sparsity; no trained weights)",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
+                   "cap": wl.cap, "path": "twell_ffn_decode", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "decode step (gate, packing, gather, reduction)",
+                     "achieved": round(alg / (ms_ev * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(alg / (ms_ev * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": alg},
+        "step_ms_events": round(ms_ev, 4),
+        "batch_path_ms": round(ms_batch, 4),
+        "workload_stats": {"nnz": nnz, "n_ovf": n_ovf},
+    }
+    if not args.no_dense:
+        def dense_step():
+            h = torch.relu(torch.matmul(x, wg.t())) * torch.matmul(x, wu.t())
+            return torch.matmul(h, wd)
+        _, dms = timed(dense_step, args.steps)
+        out["dense_bf16_ffn"] = {"ms_per_step": round(dms, 4), "sparse_speedup": round(dms / ms_ev, 3)}
+    print(json.dumps(out), flush=True)
 
 
 def run_stack(args, tw, torch, np):

@@ -175,6 +175,30 @@ TWELL_API int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const 
 TWELL_API int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
                      int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace twell_ffn_decode needs for these sizes (0 when
+ * the sizes are outside its range). */
+TWELL_API size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t tile_w);
+
+/* The whole FFN for decode-shaped calls, T <= 64 rows, bf16 (sections
+ * 2.1-2.3 of the page: the same gate, TwELL, overflow partition and fused
+ * up/down, organised for a few tokens: the gate spread over F/32 workgroups,
+ * and every row's entries cut into chunks shared out over the GPU so that a
+ * heavy row does not run alone).  Writes everything twell_pack_gate_hybrid
+ * writes (TwELL, row_ovf, ovf_rows, n_ovf, the dense backup of the first
+ * min(n_ovf, max_ovf) overflow rows, order) and every row of y, overflow rows
+ * included (whatever max_ovf is): y[t] = sum over t's active neurons j, in
+ * ascending j, of (h * (x[t] . W_u^T[j])) * W_d[j], h the stored bf16 gate
+ * value, in fp32.  Same bits for repeated calls.
+ *   x : device [T][d] bf16; wg_t, wu_t, wd : device [F][d] bf16; y : [T][d] float.
+ *   hy : T <= 64, vdtype TWELL_BF16, T * F <= 2^20, F / tile_w <= 512.
+ *   workspace : device, >= twell_ffn_decode_workspace_bytes(T, F, d, tile_w),
+ *               256-byte aligned, content ignored on entry.
+ * Returns TWELL_OK, TWELL_E_UNSUPPORTED outside that range, or another
+ * negative twell_status. */
+TWELL_API int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                               const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* Static text for a status code. */
 TWELL_API const char *twell_status_str(int status);
 

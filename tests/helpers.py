@@ -87,6 +87,72 @@ def run_hip(wl, max_ovf=None, stream=None, unaligned=False):
     }
 
 
+def run_decode(wl, max_ovf=None, stream=None, unaligned=False, calls=1):
+    """Run twell_ffn_decode `calls` times (poisoned outputs and workspace before
+    the first); return host arrays of the last call plus every call's y."""
+    import torch
+    import unstructured_sparse_transformer_amd as tw
+    dt, x, wg, wu, wd = to_device(wl)
+    if max_ovf is None:
+        max_ovf = wl.T
+    hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
+    if unaligned:
+        _offset_views(hy, dt)
+    hy.ell.cnt.fill_(-7)
+    hy.ell.idx.fill_(0xAB)
+    hy.ell.val.fill_(-3.0)
+    hy.row_ovf.fill_(-7)
+    hy.n_ovf.fill_(-7)
+    hy.order.fill_(-7)
+    if max_ovf:
+        hy.ovf_rows.fill_(-7)
+        hy.dense.fill_(-5.0)
+    ws = tw.decode_workspace(wl.T, wl.F, wl.d, wl.tile_w)
+    ws.fill_(0xCD)  # content is ignored on entry
+    ys = []
+    for _ in range(calls):
+        y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+        tw.twell_ffn_decode(x, wg, wu, wd, hy, y, ws, stream)
+        ys.append(y)
+    torch.cuda.synchronize()
+    n_ovf = int(hy.n_ovf.item())
+    m = min(n_ovf, max_ovf)
+    return {
+        "cnt": hy.ell.cnt.cpu().numpy(),
+        "val": hy.ell.val.float().cpu().numpy(),
+        "idx": hy.ell.idx.cpu().numpy(),
+        "row_ovf": hy.row_ovf.cpu().numpy(),
+        "n_ovf": n_ovf,
+        "ovf_rows": hy.ovf_rows[:m].cpu().numpy(),
+        "dense": hy.dense[:m].float().cpu().numpy(),
+        "y": ys[-1].cpu().numpy(),
+        "ys": [a.cpu().numpy() for a in ys],
+        "order": hy.order.cpu().numpy(),
+        "max_ovf": max_ovf,
+    }
+
+
+def compare_decode(wl, out, label=""):
+    """TwELL, partition, dense backup and order as for the batch path; every
+    row of y (overflow rows included) within Y_RTOL of the exact-h oracle and
+    within Y_RTOL_STORED of the stored-h oracle; repeated calls bit-identical."""
+    ref = compare(wl, out, check_y=False, label=label)
+    y = out["y"].astype(np.float64)
+    assert np.isfinite(y).all(), f"{label}: non-finite y"
+    num, den = row_rel_err(y, ref.y_exact)
+    zero = den == 0
+    assert not y[zero].any(), f"{label}: rows without actives must be exactly 0"
+    bad = ~zero & (num > Y_RTOL * den)
+    assert not bad.any(), f"{label}: y rows off by more than {Y_RTOL}: {np.nonzero(bad)[0][:10]}"
+    num2, den2 = row_rel_err(y, ref.y_stored)
+    nz = den2 > 0
+    assert (num2[nz] <= Y_RTOL_STORED * den2[nz]).all(), \
+        f"{label}: y vs stored-h oracle: max rel {np.max(num2[nz] / den2[nz]):.3g}"
+    for k, yk in enumerate(out["ys"][:-1]):
+        np.testing.assert_array_equal(yk, out["y"], err_msg=f"{label}: call {k} differs from the last call")
+    return ref
+
+
 # Work classes of the fused step's schedule (the C header's definition):
 # stored entries e >= 256, 192..255, 128..191, 64..127, 32..63, 16..31, 1..15, 0.
 WORK_EDGES = (1, 16, 32, 64, 128, 192, 256)

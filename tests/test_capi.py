@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 101
+    assert lib.twell_version() == 102
 
 
 def test_status_strings():
@@ -101,6 +101,29 @@ def test_fused_and_hybrid_validation():
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, ctypes.byref(odd), None) == -2
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, None, None) == -1
     assert lib.twell_ffn_hybrid_workspace_bytes(0, 512, 64, 1) == 0
+
+
+def test_ffn_decode_validation():
+    lib = tw.load()
+    f = lib.twell_ffn_decode
+    hy = lambda **k: tw.TwellHybridT(_desc(**k), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)  # noqa: E731
+    need = lib.twell_ffn_decode_workspace_bytes(16, 512, 64, 128)
+    assert need > 16 * 512 * 4
+    assert lib.twell_ffn_decode_workspace_bytes(65, 512, 64, 128) == 0      # T > 64
+    assert lib.twell_ffn_decode_workspace_bytes(16, 512, 64, 100) == 0      # tile width
+    ok = hy()
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, None, GOOD, GOOD, need, None) == -1
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(ok), GOOD, None, need, None) == -1        # workspace NULL
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(ok), GOOD, GOOD + 16, need, None) == -2   # not 256-aligned
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(ok), GOOD, GOOD, need - 1, None) == -6
+    assert f(GOOD, GOOD, None, GOOD, 64, ctypes.byref(ok), GOOD, GOOD, need, None) == -1        # W_u NULL
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(ok), GOOD + 4, GOOD, need, None) == -2    # y misaligned
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(hy(T=65)), GOOD, GOOD, need, None) == -4  # T > 64
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(hy(vd=0)), GOOD, GOOD, need, None) == -4  # fp32
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(hy(T=64, F=32768, w=256)), GOOD, GOOD, need,
+             None) == -4                                                                        # T * F > 2^20
+    assert f(GOOD, GOOD, GOOD, GOOD, 60, ctypes.byref(ok), GOOD, GOOD, need, None) == -3        # d % 64
+    assert f(None, None, None, None, 64, ctypes.byref(hy(T=0)), None, None, 0, None) == 0       # nothing to do
 
 
 def test_binding_requires_library(tmp_path, monkeypatch):

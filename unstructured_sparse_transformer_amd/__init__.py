@@ -8,7 +8,8 @@ raises when the library is missing, and every call raises on a non-OK status.
 The functions carry the C names (``include/twell.h``):
 ``twell_pack_gate``, ``twell_pack_gate_stats``, ``twell_partition_overflow``, ``twell_pack_gate_hybrid``,
 ``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
-``twell_ffn_hybrid_workspace_bytes``.
+``twell_ffn_hybrid_workspace_bytes``, ``twell_ffn_decode``,
+``twell_ffn_decode_workspace_bytes``.
 """
 
 from __future__ import annotations
@@ -24,8 +25,8 @@ TWELL_F32, TWELL_BF16 = 0, 1
 STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_SHAPE",
           -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE"}
 EXPORTS = ("twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
-           "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid", "twell_status_str",
-           "twell_version")
+           "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
+           "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_status_str", "twell_version")
 
 
 class TwellT(ctypes.Structure):
@@ -69,11 +70,14 @@ def load(path: str = LIB_PATH):
     lib.twell_ffn_hybrid_workspace_bytes.restype = ctypes.c_size_t
     lib.twell_ffn_hybrid.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
     lib.twell_ffn_overflow.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
+    lib.twell_ffn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.twell_ffn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.twell_ffn_decode.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P, ctypes.c_size_t, P]
     lib.twell_status_str.argtypes = [ctypes.c_int]
     lib.twell_status_str.restype = ctypes.c_char_p
     lib.twell_version.restype = ctypes.c_int
     for fn in (lib.twell_pack_gate, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
-               lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow):
+               lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_decode):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -214,6 +218,25 @@ def twell_ffn_overflow(hy: Hybrid, x, wu_t, wd, y, workspace, stream=None):
     _check("twell_ffn_overflow",
            lib.twell_ffn_overflow(ctypes.byref(hy.desc()), _ptr(x), _ptr(wu_t), _ptr(wd), int(x.shape[1]),
                                   _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def twell_ffn_decode_workspace_bytes(T: int, F: int, d: int, tile_w: int) -> int:
+    return int(load().twell_ffn_decode_workspace_bytes(T, F, d, tile_w))
+
+
+def twell_ffn_decode(x, wg_t, wu_t, wd, hy: Hybrid, y, workspace, stream=None):
+    lib = load()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("twell_ffn_decode",
+           lib.twell_ffn_decode(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), int(x.shape[1]), ctypes.byref(hy.desc()),
+                                _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def decode_workspace(T: int, F: int, d: int, tile_w: int, device="cuda"):
+    """A workspace tensor of the size twell_ffn_decode needs (256-byte aligned by the allocator)."""
+    import torch
+    n = twell_ffn_decode_workspace_bytes(T, F, d, tile_w)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def hybrid_workspace(max_ovf: int, F: int, d: int, dtype, device="cuda"):

@@ -97,7 +97,7 @@ size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
 
 extern "C" {
 
-int twell_version(void) { return 101; }
+int twell_version(void) { return 102; }
 
 const char *twell_status_str(int status)
 {
@@ -181,6 +181,48 @@ int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d, const twe
     TWELL_TRY(check_hybrid(hy));
     TWELL_TRY(twell_pack_gate(x, wg_t, d, &hy->ell, stream));
     return twell_partition_overflow(x, wg_t, d, hy, stream);
+}
+
+size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t tile_w)
+{
+    if (T < 0 || T > twell::DEC_MAX_T || F <= 0 || d <= 0 || (tile_w != 32 && tile_w != 64 && tile_w != 128 &&
+                                                             tile_w != 256) || F % tile_w != 0)
+        return 0;
+    return twell::decode_ws_layout(nullptr, T, F, tile_w, d).bytes;
+}
+
+int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                     const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *h = &hy->ell;
+    TWELL_TRY(check_layout(h, d));
+    TWELL_TRY(check_hybrid(hy));
+    if (h->vdtype != TWELL_BF16 || h->T > twell::DEC_MAX_T || (int64_t)h->T * h->F > twell::DEC_MAX_TF ||
+        h->F / h->tile_w > twell::DEC_MAX_NB)
+        return TWELL_E_UNSUPPORTED;
+    if (h->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wg_t));
+    TWELL_TRY(check_mat(wu_t));
+    TWELL_TRY(check_mat(wd));
+    TWELL_TRY(check_mat(y));
+    TWELL_TRY(check_ptrs(h));
+    if (!workspace)
+        return TWELL_E_NULL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return TWELL_E_ALIGN;
+    const twell::DecodeWs w = twell::decode_ws_layout(workspace, h->T, h->F, h->tile_w, d);
+    if (workspace_bytes < w.bytes)
+        return TWELL_E_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TWELL_TRY(hip_status(twell::launch_decode_gate_pack(x, wg_t, h->T, d, h->F, h->tile_w, h->cap, h->val, h->idx,
+                                                        h->cnt, hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->order,
+                                                        hy->max_ovf, w, s)));
+    return hip_status(twell::launch_ffn_decode(h->cnt, h->val, h->idx, h->T, h->F, h->tile_w, h->cap, x, wu_t, wd, d,
+                                               hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->max_ovf, hy->dense, y, w, s));
 }
 
 int twell_ffn_fused(const twell_t *h, const int32_t *order, const void *x, const void *wu_t, const void *wd,

@@ -18,6 +18,7 @@
 // dot products are reduced with DPP, and y += (h*u) * W_d[j] runs in fp32.
 // The partial rows are added in LDS in a fixed order: no atomics, and the
 // result does not depend on timing.
+#include "decode.h"
 #include "launch.h"
 #include "twell_device.h"
 
@@ -331,6 +332,232 @@ hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, con
     if (vdtype == 1)
         return fused_dispatch<__bf16>(cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, s);
     return fused_dispatch<float>(cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, s);
+}
+
+// ------------------------------------------------------------------ decode-shaped calls
+// The same per-entry work for T <= 64, cut into chunks of CE consecutive
+// entries of a row (row order: tiles ascending, slots ascending; a row's
+// entries are all its active neurons, CE from the packing kernel), so that a
+// heavy row is spread over many waves instead of trailing in one workgroup.
+// One wave per chunk: it lists the chunk's (j, h) in LDS -- from the TwELL
+// slots for a row that fits (binary search of each entry's tile in the row's
+// tile prefix), from z for an overflow row (one pass per tile the chunk
+// touches, values rounded to bf16 as the dense backup stores them) -- streams
+// the entries as the batch kernel does and writes its partial y row.  The
+// partial rows of a row are added in chunk order by chunk_reduce_kernel.
+struct ChunkArgs {
+    FusedArgs<__bf16> f;        // x, wu_t, wd, d, nchunks, T, F, tile_w, n_b, cap, cnt, val, idx
+    const float *z;             // [T][F]
+    const int32_t *row_ovf, *row_e, *chunk0, *chunk_e;
+    float *part;                // [chunks][d]
+};
+
+template <int NC>
+__global__ __launch_bounds__(256) void ffn_chunks_kernel(ChunkArgs a)
+{
+    constexpr int E = Elt<__bf16>::PER_CHUNK;
+    constexpr int PMAX = DEC_MAX_NB + 1;  // tile prefix entries held in LDS
+    __shared__ int2 clist[4][DEC_MAX_E];
+    __shared__ int spre[4][PMAX];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = a.f.T, n_b = a.f.n_b, w = a.f.tile_w, cap = a.f.cap;
+    const int n_chunks = a.chunk0[T];
+    const int CE = *a.chunk_e;
+    const int64_t row_bytes = (int64_t)a.f.d * Elt<__bf16>::SIZE;
+    int2 *list = clist[wave];
+    int *sp = spre[wave];
+    for (int c = blockIdx.x * 4 + wave; c < n_chunks; c += gridDim.x * 4) {
+        // the chunk's row: rows whose first chunk is <= c, minus one (chunk0 ascends)
+        const int le = __popcll(__ballot(lane < T && a.chunk0[lane] <= c));
+        const int t = __builtin_amdgcn_readfirstlane(le - 1);
+        // exclusive prefix of the row's tile counts: sp[b] = entries before tile b
+        const int32_t *crow = a.f.cnt + (int64_t)t * n_b;
+        int run = 0;
+        for (int b0 = 0; b0 < n_b; b0 += 64) {
+            const int b = b0 + lane;
+            const int v = b < n_b ? crow[b] : 0;
+            const int incl = wave_incl_scan(v, lane);
+            if (b < n_b)
+                sp[b] = run + incl - v;
+            run += __shfl(incl, 63, 64);
+        }
+        if (lane == 0)
+            sp[n_b] = run;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        const int e_t = sp[n_b];
+        const int k0 = (c - a.chunk0[t]) * CE;
+        const int n = CE < e_t - k0 ? CE : e_t - k0;
+        if (!a.row_ovf[t]) {
+            // every entry is a TwELL slot: entry k sits in the last tile b with sp[b] <= k
+            for (int p = lane; p < n; p += 64) {
+                const int k = k0 + p;
+                int lo = 0, hi = n_b - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (sp[mid] <= k)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                const int64_t slot = ((int64_t)t * n_b + lo) * cap + (k - sp[lo]);
+                int j = lo * w + a.f.idx[slot];
+                j = j < a.f.F ? j : a.f.F - 1;  // memory safety for a corrupt index
+                list[p] = make_int2(j, __float_as_int(load_elem(a.f.val + slot)));
+            }
+        } else {
+            // an overflow row: its entries are all active columns, taken from z
+            int b = 0;
+            {
+                int lo = 0, hi = n_b - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (sp[mid] <= k0)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                b = lo;
+            }
+            for (; b < n_b && sp[b] < k0 + n; ++b) {
+                const float *zt = a.z + (int64_t)t * a.f.F + (int64_t)b * w;
+                int base = sp[b];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int col = lane + 64 * jj;
+                    const float v = col < w ? zt[col] : 0.f;
+                    const uint64_t bal = __ballot(col < w && v > 0.f);
+                    const int k = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                    if (((bal >> lane) & 1ull) && k >= k0 && k < k0 + n)
+                        list[k - k0] = make_int2(b * w + col, __float_as_int((float)(__bf16)v));
+                    base += __popcll(bal);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's list stores are done
+        __builtin_amdgcn_wave_barrier();
+
+        float xf[NC][E], yacc[NC][E];
+        const char *xrow = (const char *)a.f.x + (int64_t)t * row_bytes;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const int ch = lane + 64 * cc;
+            const u32x4 v = ch < a.f.nchunks ? ldg16(xrow + ch * 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                xf[cc][e] = chunk_elem<__bf16>(v, e);
+                yacc[cc][e] = 0.f;
+            }
+        }
+        const int ngroups = n / FUSED_G;
+        group_stream<__bf16, NC, FUSED_G>(a.f, list, 0, 1, ngroups, lane, row_bytes, xf, yacc);
+        for (int e0 = ngroups * FUSED_G; e0 < n; ++e0) {
+            Group<__bf16, NC, 1> g1;
+            group_load<__bf16, NC, 1>(a.f, list, e0, lane, row_bytes, g1);
+            group_apply<__bf16, NC, 1>(g1, xf, yacc);
+        }
+        float *pr = a.part + (int64_t)c * a.f.d;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const int ch = lane + 64 * cc;
+            if (ch < a.f.nchunks) {
+                *reinterpret_cast<float4 *>(pr + ch * E) =
+                    make_float4(yacc[cc][0], yacc[cc][1], yacc[cc][2], yacc[cc][3]);
+                *reinterpret_cast<float4 *>(pr + ch * E + 4) =
+                    make_float4(yacc[cc][4], yacc[cc][5], yacc[cc][6], yacc[cc][7]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();  // list and prefix reads done before the next chunk's stores
+    }
+}
+
+// y[t] = sum of row t's partial rows (0 for a row without entries), in a
+// fixed order: one workgroup per (row, 256 columns); its 4 waves each add every
+// 4th chunk in chunk order, two loads in flight, and the 4 sums meet in LDS in
+// wave order.  Blocks past the rows write the dense backup rows ReLU(z) (bf16)
+// of the first min(n_ovf, max_ovf) overflow rows.
+__global__ __launch_bounds__(256) void chunk_reduce_kernel(const float *part, const int32_t *chunk0, int T, int d,
+                                                           float *y, const float *z, int F, const int32_t *ovf_rows,
+                                                           const int32_t *n_ovf, int max_ovf, __bf16 *dense)
+{
+    __shared__ float4 sred[4][64];
+    const int cpr = (d + 255) / 256;  // column slices per row (d is a multiple of 64)
+    const int r = blockIdx.x / cpr;
+    if (r < T) {
+        const int tid = threadIdx.x, g = tid >> 6, l = tid & 63;
+        const int col = (blockIdx.x - r * cpr) * 256 + 4 * l;
+        const int c0 = chunk0[r];
+        const int c1 = col < d ? chunk0[r + 1] : c0;  // columns past d: nothing to add
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        int c = c0 + g;
+        for (; c + 4 < c1; c += 8) {
+            const float4 p = *reinterpret_cast<const float4 *>(part + (int64_t)c * d + col);
+            const float4 q = *reinterpret_cast<const float4 *>(part + (int64_t)(c + 4) * d + col);
+            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+            s.x += q.x; s.y += q.y; s.z += q.z; s.w += q.w;
+        }
+        if (c < c1) {
+            const float4 p = *reinterpret_cast<const float4 *>(part + (int64_t)c * d + col);
+            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+        }
+        sred[g][l] = s;
+        __syncthreads();
+        if (g == 0 && col < d) {
+            float4 o = sred[0][l];
+#pragma unroll
+            for (int k = 1; k < 4; ++k) {
+                const float4 p = sred[k][l];
+                o.x += p.x; o.y += p.y; o.z += p.z; o.w += p.w;
+            }
+            *reinterpret_cast<float4 *>(y + (int64_t)r * d + col) = o;
+        }
+        return;
+    }
+    const int i = blockIdx.x - T * cpr;
+    const int nv = *n_ovf < max_ovf ? *n_ovf : max_ovf;
+    if (i >= nv)
+        return;
+    const float *zr = z + (int64_t)ovf_rows[i] * F;
+    for (int j = threadIdx.x; j < F; j += 256) {
+        const float v = zr[j];
+        store_elem(dense + (int64_t)i * F + j, v > 0.f ? v : 0.f);
+    }
+}
+
+hipError_t launch_ffn_decode(const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F, int tile_w,
+                             int cap, const void *x, const void *wu_t, const void *wd, int d, const int32_t *row_ovf,
+                             const int32_t *ovf_rows, const int32_t *n_ovf, int max_ovf, void *dense, float *y,
+                             const DecodeWs &w, hipStream_t s)
+{
+    ChunkArgs a{};
+    a.f = FusedArgs<__bf16>{cnt, static_cast<const __bf16 *>(val), idx, nullptr, T, F / tile_w, tile_w, cap, F,
+                            static_cast<const __bf16 *>(x), static_cast<const __bf16 *>(wu_t),
+                            static_cast<const __bf16 *>(wd), d, d * 2 / 16, y};
+    a.z = w.z;
+    a.row_ovf = row_ovf;
+    a.row_e = w.row_e;
+    a.chunk0 = w.chunk0;
+    a.chunk_e = w.chunk_e;
+    a.part = w.part;
+    const dim3 grid(DEC_GATHER_WGS), block(256);
+    const int nch = a.f.nchunks;
+    if (nch <= 64)
+        ffn_chunks_kernel<1><<<grid, block, 0, s>>>(a);
+    else if (nch <= 128)
+        ffn_chunks_kernel<2><<<grid, block, 0, s>>>(a);
+    else if (nch <= 256)
+        ffn_chunks_kernel<4><<<grid, block, 0, s>>>(a);
+    else
+        ffn_chunks_kernel<8><<<grid, block, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int dense_blocks = T < max_ovf ? T : max_ovf;
+    chunk_reduce_kernel<<<dim3(T * ((d + 255) / 256) + dense_blocks), dim3(256), 0, s>>>(
+        w.part, w.chunk0, T, d, y, w.z, F, ovf_rows, n_ovf, max_ovf, static_cast<__bf16 *>(dense));
+    return hipGetLastError();
 }
 
 }  // namespace twell

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "decode.h"
+
 namespace twell {
 
 // Gate GEMM + TwELL epilogue over all T rows.
@@ -46,6 +48,20 @@ hipError_t launch_down(int vdtype, const void *p, const void *wd, const int32_t 
 hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, const int32_t *order,
                             int T, int F, int tile_w, int cap, const void *x, const void *wu_t, const void *wd, int d,
                             float *y, hipStream_t s);
+
+// Decode-shaped calls (T <= DEC_MAX_T, bf16): gate into w.z, TwELL, overflow
+// flags / list / count, work order, and the gather's chunking.
+hipError_t launch_decode_gate_pack(const void *x, const void *wg_t, int T, int d, int F, int tile_w, int cap,
+                                   void *val, uint8_t *idx, int32_t *cnt, int32_t *row_ovf, int32_t *ovf_rows,
+                                   int32_t *n_ovf, int32_t *order, int max_ovf, const DecodeWs &w, hipStream_t s);
+
+// Decode-shaped FFN from the results of launch_decode_gate_pack: every row of
+// y (overflow rows included), and the dense backup of the first
+// min(n_ovf, max_ovf) overflow rows.
+hipError_t launch_ffn_decode(const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F, int tile_w,
+                             int cap, const void *x, const void *wu_t, const void *wd, int d, const int32_t *row_ovf,
+                             const int32_t *ovf_rows, const int32_t *n_ovf, int max_ovf, void *dense, float *y,
+                             const DecodeWs &w, hipStream_t s);
 
 // Number of split-K slabs the hybrid down projection uses for these sizes.
 int down_splits(int max_ovf, int F, int d);
