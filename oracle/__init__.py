@@ -21,14 +21,18 @@ Models", gist.science summary page):
   * x.W_u) . W_d, accumulated over neurons in ascending order in fp64.
 * ``gate_stats``: section 2.4's L1 activation penalty and dead neurons, as
   per-neuron active counts and per (row, tile) sums of the active gate values.
+* ``hybrid_to_dense``: section 2.4's hybrid-to-dense conversion; the
+  dense-to-hybrid direction is ``pack_twell`` + ``partition_overflow`` +
+  ``dense_backup`` applied to a dense activation matrix.
 
 Pins (tests/test_oracle.py): pure-Python brute force on tiny inputs, all 2^8
 patterns of one 8-wide tile, a hand-worked example (tests/golden), closed forms
 (all dead; one active neuron; dense tile; identity up/down), dense == sparse
 bitwise, nonzero conservation, round trip, numpy fp64 matmul cross-check,
-bf16 rounding against torch's conversion, and for ``gate_stats`` brute force,
+bf16 rounding against torch's conversion, for ``gate_stats`` brute force,
 conservation against the TwELL counts and closed forms (all dead, all active,
-one live neuron).
+one live neuron), and for ``hybrid_to_dense`` the exact round trip through the
+dense-to-hybrid direction and a hand-built example.
 """
 
 from __future__ import annotations
@@ -167,6 +171,17 @@ def unpack_twell(tw: TwELL) -> np.ndarray:
     kept = tw.kept()
     t, b, s = np.nonzero(kept)
     out[t, b * tw.tile_w + tw.idx[t, b, s].astype(np.int64)] = tw.val[t, b, s]
+    return out
+
+
+def hybrid_to_dense(tw: TwELL, ovf_rows, dense, max_ovf: int) -> np.ndarray:
+    """Section 2.4's hybrid-to-dense conversion: [T][F] holding the TwELL
+    entries of every row, with the first max_ovf overflow rows replaced by
+    their dense backup rows (later overflow rows keep only their TwELL
+    entries: the hybrid holds nothing more of them)."""
+    out = unpack_twell(tw)
+    for i, t in enumerate(np.asarray(ovf_rows)[:max_ovf]):
+        out[int(t)] = np.asarray(dense[i], np.float64)
     return out
 
 

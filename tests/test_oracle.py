@@ -283,3 +283,41 @@ def test_gate_stats_closed_forms():
     assert cnt[7] == T and cnt.sum() == T
     np.testing.assert_array_equal(l1[:, 0], np.arange(1, T + 1))
     assert not l1[:, 1:].any()
+
+
+# ------------------------------------------------------------ hybrid <-> dense conversions
+def test_hybrid_to_dense_hand_example():
+    """w = 4, cap = 2: row 0 fits (2 and 1 actives), row 1 overflows (3 actives
+    in tile 0), row 2 overflows too; max_ovf = 1 serves only row 1."""
+    h = np.array([[0.0, 1.5, 0.0, 2.0, 0.0, 0.0, 0.0, 3.0],
+                  [4.0, 5.0, 6.0, 0.0, 0.0, 0.0, 7.0, 0.0],
+                  [0.0, 1.0, 1.0, 1.0, 0.0, 0.0, 0.0, 0.0]])
+    tw = oracle.pack_twell(h, 4, 2, "f32")
+    row_ovf, rows, n = oracle.partition_overflow(tw.cnt, 2)
+    assert list(row_ovf) == [0, 1, 1] and list(rows) == [1, 2] and n == 2
+    dense = oracle.dense_backup(h, rows, "f32")
+    out = oracle.hybrid_to_dense(tw, rows, dense, max_ovf=1)
+    np.testing.assert_array_equal(out[0], h[0])
+    np.testing.assert_array_equal(out[1], h[1])
+    # row 2 is not served: only its first two actives of tile 0 survive
+    np.testing.assert_array_equal(out[2], [0.0, 1.0, 1.0, 0.0, 0.0, 0.0, 0.0, 0.0])
+
+
+@pytest.mark.parametrize("w,cap", [(32, 2), (64, 8), (256, 16)])
+def test_dense_hybrid_round_trip(w, cap):
+    """dense -> hybrid -> dense gives back max(H, 0) exactly when every
+    overflow row is served (TwELL keeps a fitting row whole, the dense backup
+    keeps an overflow row whole); negative and NaN entries come back as 0."""
+    rng = np.random.default_rng(w + cap)
+    T, F = 40, 512
+    h = oracle.store_round(rng.standard_normal((T, F)) * (rng.random((T, F)) < 0.08), "bf16")
+    h[3, :200] = np.abs(h[3, :200]) + 0.5  # a heavy row
+    h = oracle.store_round(h, "bf16")
+    h[5, 7] = np.nan
+    tw = oracle.pack_twell(h, w, cap, "bf16")
+    _, rows, n = oracle.partition_overflow(tw.cnt, cap)
+    assert n > 0
+    dense = oracle.dense_backup(h, rows, "bf16")
+    out = oracle.hybrid_to_dense(tw, rows, dense, max_ovf=n)
+    want = np.where(h > 0, h, 0.0)
+    np.testing.assert_array_equal(out, want)
