@@ -175,6 +175,25 @@ TWELL_API int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const 
 TWELL_API int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
                      int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Dense activations to the hybrid (section 2.4 of the page: the conversion
+ * kernels training uses in the forward and backward passes).  h : device
+ * [T][F], vdtype hy->ell.vdtype, row-major, 16-byte aligned.  Writes the
+ * TwELL of h (an entry is active iff h > 0: 0, -0, negatives and NaN are not;
+ * the same packing rules as twell_pack_gate), row_ovf, ovf_rows, n_ovf,
+ * order (as twell_partition_overflow), and dense[i] = max(h[ovf_rows[i]], 0)
+ * for the first min(n_ovf, max_ovf) overflow rows.  The hybrid of a
+ * non-negative h with every overflow row served holds h exactly. */
+TWELL_API int twell_dense_to_hybrid(const void *h, const twell_hybrid_t *hy, void *stream);
+
+/* The hybrid to dense activations (section 2.4 of the page).  out : device
+ * [T][F], vdtype hy->ell.vdtype, 16-byte aligned, every element written: each
+ * row holds its kept TwELL entries and zeros elsewhere, except the first
+ * min(n_ovf, max_ovf) overflow rows, which are their dense backup rows
+ * (later overflow rows keep only their TwELL entries: the hybrid holds
+ * nothing more of them).  Expects hy as written by twell_dense_to_hybrid,
+ * twell_pack_gate_hybrid or twell_ffn_decode. */
+TWELL_API int twell_hybrid_to_dense(const twell_hybrid_t *hy, void *out, void *stream);
+
 /* Bytes of device workspace twell_ffn_decode needs for these sizes (0 when
  * the sizes are outside its range). */
 TWELL_API size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t tile_w);

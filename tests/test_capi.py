@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 102
+    assert lib.twell_version() == 103
 
 
 def test_status_strings():
@@ -124,6 +124,26 @@ def test_ffn_decode_validation():
              None) == -4                                                                        # T * F > 2^20
     assert f(GOOD, GOOD, GOOD, GOOD, 60, ctypes.byref(ok), GOOD, GOOD, need, None) == -3        # d % 64
     assert f(None, None, None, None, 64, ctypes.byref(hy(T=0)), None, None, 0, None) == 0       # nothing to do
+
+
+def test_conversion_validation():
+    lib = tw.load()
+    hy = tw.TwellHybridT(_desc(), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
+    assert lib.twell_dense_to_hybrid(GOOD, None, None) == -1
+    assert lib.twell_dense_to_hybrid(None, ctypes.byref(hy), None) == -1
+    assert lib.twell_dense_to_hybrid(GOOD + 2, ctypes.byref(hy), None) == -2
+    bad = tw.TwellHybridT(_desc(w=100), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
+    assert lib.twell_dense_to_hybrid(GOOD, ctypes.byref(bad), None) == -4
+    nod = tw.TwellHybridT(_desc(), 8, 0, GOOD, GOOD, GOOD, None, GOOD)      # dense NULL with max_ovf > 0
+    assert lib.twell_dense_to_hybrid(GOOD, ctypes.byref(nod), None) == -1
+    assert lib.twell_hybrid_to_dense(None, GOOD, None) == -1
+    assert lib.twell_hybrid_to_dense(ctypes.byref(hy), None, None) == -1
+    assert lib.twell_hybrid_to_dense(ctypes.byref(hy), GOOD + 8, None) == -2
+    noval = tw.TwellHybridT(_desc(val=0), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
+    assert lib.twell_hybrid_to_dense(ctypes.byref(noval), GOOD, None) == -1
+    empty = tw.TwellHybridT(_desc(T=0), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
+    assert lib.twell_hybrid_to_dense(ctypes.byref(empty), None, None) == 0
+    assert lib.twell_dense_to_hybrid(None, ctypes.byref(empty), None) == 0
 
 
 def test_binding_requires_library(tmp_path, monkeypatch):

@@ -9,7 +9,8 @@ The functions carry the C names (``include/twell.h``):
 ``twell_pack_gate``, ``twell_pack_gate_stats``, ``twell_partition_overflow``, ``twell_pack_gate_hybrid``,
 ``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
 ``twell_ffn_hybrid_workspace_bytes``, ``twell_ffn_decode``,
-``twell_ffn_decode_workspace_bytes``.
+``twell_ffn_decode_workspace_bytes``, ``twell_dense_to_hybrid``,
+``twell_hybrid_to_dense``.
 """
 
 from __future__ import annotations
@@ -26,7 +27,8 @@ STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_S
           -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE"}
 EXPORTS = ("twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
            "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
-           "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_status_str", "twell_version")
+           "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_dense_to_hybrid", "twell_hybrid_to_dense",
+           "twell_status_str", "twell_version")
 
 
 class TwellT(ctypes.Structure):
@@ -73,11 +75,14 @@ def load(path: str = LIB_PATH):
     lib.twell_ffn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.twell_ffn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.twell_ffn_decode.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P, ctypes.c_size_t, P]
+    lib.twell_dense_to_hybrid.argtypes = [P, ctypes.POINTER(TwellHybridT), P]
+    lib.twell_hybrid_to_dense.argtypes = [ctypes.POINTER(TwellHybridT), P, P]
     lib.twell_status_str.argtypes = [ctypes.c_int]
     lib.twell_status_str.restype = ctypes.c_char_p
     lib.twell_version.restype = ctypes.c_int
     for fn in (lib.twell_pack_gate, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
-               lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_decode):
+               lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_decode,
+               lib.twell_dense_to_hybrid, lib.twell_hybrid_to_dense):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -218,6 +223,16 @@ def twell_ffn_overflow(hy: Hybrid, x, wu_t, wd, y, workspace, stream=None):
     _check("twell_ffn_overflow",
            lib.twell_ffn_overflow(ctypes.byref(hy.desc()), _ptr(x), _ptr(wu_t), _ptr(wd), int(x.shape[1]),
                                   _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def twell_dense_to_hybrid(h, hy: Hybrid, stream=None):
+    """h: [T][F] in the hybrid's value dtype."""
+    _check("twell_dense_to_hybrid", load().twell_dense_to_hybrid(_ptr(h), ctypes.byref(hy.desc()), _stream(stream)))
+
+
+def twell_hybrid_to_dense(hy: Hybrid, out, stream=None):
+    """out: [T][F] in the hybrid's value dtype (every element written)."""
+    _check("twell_hybrid_to_dense", load().twell_hybrid_to_dense(ctypes.byref(hy.desc()), _ptr(out), _stream(stream)))
 
 
 def twell_ffn_decode_workspace_bytes(T: int, F: int, d: int, tile_w: int) -> int:

@@ -97,7 +97,7 @@ size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
 
 extern "C" {
 
-int twell_version(void) { return 102; }
+int twell_version(void) { return 103; }
 
 const char *twell_status_str(int status)
 {
@@ -181,6 +181,38 @@ int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d, const twe
     TWELL_TRY(check_hybrid(hy));
     TWELL_TRY(twell_pack_gate(x, wg_t, d, &hy->ell, stream));
     return twell_partition_overflow(x, wg_t, d, hy, stream);
+}
+
+int twell_dense_to_hybrid(const void *h, const twell_hybrid_t *hy, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *e = &hy->ell;
+    TWELL_TRY(check_layout(e, 64));
+    TWELL_TRY(check_hybrid(hy));
+    if (e->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(h));
+    TWELL_TRY(check_ptrs(e));
+    return hip_status(twell::launch_dense_to_hybrid(e->vdtype, h, e->T, e->F, e->tile_w, e->cap, e->val, e->idx,
+                                                    e->cnt, hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->order,
+                                                    hy->max_ovf, hy->dense, static_cast<hipStream_t>(stream)));
+}
+
+int twell_hybrid_to_dense(const twell_hybrid_t *hy, void *out, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *e = &hy->ell;
+    TWELL_TRY(check_layout(e, 64));
+    TWELL_TRY(check_hybrid(hy));
+    if (e->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(out));
+    TWELL_TRY(check_ptrs(e));
+    return hip_status(twell::launch_hybrid_to_dense(e->vdtype, e->cnt, e->val, e->idx, e->T, e->F, e->tile_w, e->cap,
+                                                    hy->ovf_rows, hy->n_ovf, hy->max_ovf, hy->dense, out,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t tile_w)

@@ -63,6 +63,18 @@ hipError_t launch_ffn_decode(const int32_t *cnt, const void *val, const uint8_t 
                              const int32_t *ovf_rows, const int32_t *n_ovf, int max_ovf, void *dense, float *y,
                              const DecodeWs &w, hipStream_t s);
 
+// Dense activations h [T][F] -> hybrid: TwELL (active iff h > 0), overflow
+// flags / list / count, work order, dense backup rows max(h, 0).
+hipError_t launch_dense_to_hybrid(int vdtype, const void *h, int T, int F, int tile_w, int cap, void *val,
+                                  uint8_t *idx, int32_t *cnt, int32_t *row_ovf, int32_t *ovf_rows, int32_t *n_ovf,
+                                  int32_t *order, int max_ovf, void *dense, hipStream_t s);
+
+// Hybrid -> dense out [T][F]: every row from its TwELL slots, then the first
+// min(n_ovf, max_ovf) overflow rows from the dense backup.
+hipError_t launch_hybrid_to_dense(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F,
+                                  int tile_w, int cap, const int32_t *ovf_rows, const int32_t *n_ovf, int max_ovf,
+                                  const void *dense, void *out, hipStream_t s);
+
 // Number of split-K slabs the hybrid down projection uses for these sizes.
 int down_splits(int max_ovf, int F, int d);
 
