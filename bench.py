@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-energy", action="store_true", help="skip the energy-per-token measurement")
     ap.add_argument("--no-stats", action="store_true", help="skip the gate-statistics variant timing")
+    ap.add_argument("--no-conversions", action="store_true", help="skip the hybrid <-> dense conversion timing")
     ap.add_argument("--batch-path", action="store_true",
                     help="decode-shaped workloads (T <= 64): time the batch path instead of twell_ffn_decode")
     ap.add_argument("--energy-seconds", type=float, default=2.0, help="run time per energy measurement")
@@ -322,6 +323,34 @@ def main():
                              "pack_gate_stats_ms": round(s_ms, 4), "overhead_frac": round(s_ms / p_ms - 1, 4),
                              "dead_neurons": int((ncnt == 0).sum().item()),
                              "mean_l1_per_token": round(float(l1.sum(1).mean().item()), 4)}
+
+    # ---- hybrid <-> dense conversions of this layer's activations (the training
+    # kernels), HBM-bound: algorithmic bytes = the dense side (T x F elements)
+    # plus the TwELL and dense-backup side
+    if not args.no_conversions:
+        dense_h = torch.empty((wl.T, wl.F), dtype=dt, device=dev)
+        hc = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
+        tw.twell_hybrid_to_dense(hy, dense_h)
+        tw.twell_dense_to_hybrid(dense_h, hc)
+        torch.cuda.synchronize()
+        conv = {}
+        side = int(wl.T * n_b * (4 + wl.cap * (esz + 1)) + n_ovf * wl.F * esz)
+        for name, fn, nbytes in (("hybrid_to_dense", lambda: tw.twell_hybrid_to_dense(hy, dense_h),
+                                  wl.T * wl.F * esz + side),
+                                 ("dense_to_hybrid", lambda: tw.twell_dense_to_hybrid(dense_h, hc),
+                                  wl.T * wl.F * esz + side)):
+            evc = [(DevEvent(), DevEvent()) for _ in range(args.steps)]
+            for e in evc:
+                e[0].record()
+                fn()
+                e[1].record()
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in evc]))
+            conv[name] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes,
+                          "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        out["conversions"] = conv
+        del dense_h, hc
 
     # ---- cold-cache variant: flush MALL/L2 with a 1 GiB write between steps (outside the events)
     if not args.no_cold:

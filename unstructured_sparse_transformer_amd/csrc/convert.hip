@@ -6,16 +6,18 @@
 // and needs kernels that turn a dense matrix into the hybrid and back, in the
 // forward and the backward pass.  Both directions are streaming kernels bound
 // by HBM (the dense side is T x F elements):
-//   dense -> hybrid: one workgroup per row; each wave packs TwELL tiles with
-//     the same ballot / mbcnt rules as the gate epilogue (active iff h > 0,
-//     ascending columns, true count kept, first cap values stored, zero
-//     padding); the overflow flags, list and work order then come from the
-//     batch path's partition kernels, and the dense backup rows are the
-//     overflow rows' max(h, 0).
-//   hybrid -> dense: one workgroup per row; each wave expands a tile through a
-//     per-wave LDS row (zeros, then the kept slots scattered by column) and
-//     writes it with coalesced stores; a second kernel overwrites the first
-//     min(n_ovf, max_ovf) overflow rows with their dense backup rows.
+//   dense -> hybrid: one workgroup per row, 16 bytes of the row per lane; the
+//     TwELL rules are the gate epilogue's (active iff h > 0, ascending
+//     columns, true count kept, first cap values stored, zero padding), with
+//     slots from a segmented scan over each tile's lanes, and the row's
+//     overflow flag and work value written by its workgroup; the ascending
+//     overflow list and work order then come from the batch path's compaction
+//     kernel, and the dense backup rows are the overflow rows' max(h, 0).
+//   hybrid -> dense: one workgroup per row; each wave expands whole tiles
+//     through a per-wave LDS row (zeros, then the kept slots scattered by
+//     column) and writes it with 16-byte stores; a second kernel overwrites
+//     the first min(n_ovf, max_ovf) overflow rows with their dense backup
+//     rows.
 #include "launch.h"
 #include "twell_device.h"
 
@@ -27,62 +29,119 @@ template <typename TI> struct ConvArgs {
     TI *val;
     uint8_t *idx;
     int32_t *cnt;
+    int32_t *row_ovf, *work;  // dense -> hybrid: per-row flag and stored entries (0 if flagged)
 };
 
-// Tiles of row t, wave-strided: wave w handles tiles w, w + 8, ...; the
-// values of up to 4 tiles are requested together.
+// Inclusive scan of v over segments of L lanes (L a power of two, <= 64; gl =
+// lane within its segment): DPP row shifts inside 16-lane rows (masked at
+// segment starts when L < 16), then row broadcasts across rows.
+__device__ __forceinline__ int seg_incl_scan(int v, int gl, int L)
+{
+    int y = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += gl >= 1 ? y : 0;
+    if (L > 2) {
+        y = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+        v += gl >= 2 ? y : 0;
+    }
+    if (L > 4) {
+        y = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+        v += gl >= 4 ? y : 0;
+    }
+    if (L > 8) {
+        y = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+        v += gl >= 8 ? y : 0;
+    }
+    if (L > 16)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    if (L > 32)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+// Row t; lane l of a wave pass owns CPL = 16 / sizeof(TI) consecutive columns
+// (one 16-byte load), so a pass covers 64 * CPL columns = 64 * CPL / w whole
+// tiles, each spread over L = w / CPL consecutive lanes.  A lane's activity
+// bits give its count; a segmented scan over the L lanes of its tile gives the
+// count before it, so every active column's slot is known in ascending column
+// order.  Wave w takes passes w, w + 8, ...; up to 4 passes' loads are
+// requested together.  The row's overflow flag and stored-entry count (the
+// work order's input) are gathered with LDS atomics and written at the end.
 template <typename TI>
 __global__ __launch_bounds__(512) void dense_pack_kernel(ConvArgs<TI> a)
 {
-    constexpr int NW = 8, BATCH = 4;
+    constexpr int NW = 8, BATCH = 4, CPL = 16 / (int)sizeof(TI);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = blockIdx.x;
     const int w = a.tile_w, cap = a.cap;
-    const TI *hr = a.dense + (int64_t)t * a.F;
-    for (int b0 = wave; b0 < a.n_b; b0 += NW * BATCH) {
-        float v[BATCH][4];
+    const int L = w / CPL;                    // lanes per tile (power of two, 4..64)
+    const int gl = lane & (L - 1);            // lane within its tile
+    const int F16 = a.F / CPL;                // 16-byte chunks per row
+    const char *hr = reinterpret_cast<const char *>(a.dense + (int64_t)t * a.F);
+    __shared__ int s_stored, s_ovf;
+    if (threadIdx.x == 0) {
+        s_stored = 0;
+        s_ovf = 0;
+    }
+    __syncthreads();
+    for (int p0 = wave; p0 * 64 < F16; p0 += NW * BATCH) {
+        u32x4 v[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            const int b = b0 + u * NW;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = lane + 64 * j;
-                v[u][j] = (b < a.n_b && c < w) ? load_elem(hr + (int64_t)b * w + c) : 0.f;
-            }
+            const int ch = (p0 + u * NW) * 64 + lane;
+            v[u] = ch < F16 ? ldg16(hr + (int64_t)ch * 16) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            const int b = b0 + u * NW;
-            if (b >= a.n_b)
-                continue;
-            uint64_t bal[4];
-            int total = 0;
+            const int ch = (p0 + u * NW) * 64 + lane;  // this lane's chunk
+            if ((p0 + u * NW) * 64 >= F16)
+                break;
+            const bool live = ch < F16;
+            float x[CPL];
+            uint32_t m = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bal[j] = __ballot(lane + 64 * j < w && v[u][j] > 0.f);
-                total += __popcll(bal[j]);
+            for (int k = 0; k < CPL; ++k) {
+                x[k] = chunk_elem<TI>(v[u], k);
+                m |= (live && x[k] > 0.f) ? (1u << k) : 0u;
             }
+            const int cntl = __popc(m);
+            // segmented inclusive scan over the tile's L lanes
+            const int incl = seg_incl_scan(cntl, gl, L);
+            const int total = __shfl(incl, (lane | (L - 1)), 64);
+            const int col0 = ch * CPL;                 // first column of the lane in the row
+            const int b = col0 / w;                    // its tile
             const int64_t slot0 = ((int64_t)t * a.n_b + b) * cap;
-            int base = 0;
+            if (live) {
+                int slot = incl - cntl;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
-                                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
-                if (((bal[j] >> lane) & 1ull) && slot < cap) {
-                    store_elem(a.val + slot0 + slot, v[u][j]);
-                    a.idx[slot0 + slot] = (uint8_t)(lane + 64 * j);
+                for (int k = 0; k < CPL; ++k) {
+                    if ((m >> k) & 1u) {
+                        if (slot < cap) {
+                            store_elem(a.val + slot0 + slot, x[k]);
+                            a.idx[slot0 + slot] = (uint8_t)(gl * CPL + k);
+                        }
+                        ++slot;
+                    }
                 }
-                base += __popcll(bal[j]);
+                const int kept = total < cap ? total : cap;
+                for (int s2 = kept + gl; s2 < cap; s2 += L) {
+                    store_elem(a.val + slot0 + s2, 0.f);
+                    a.idx[slot0 + s2] = 0;
+                }
+                if (gl == 0) {
+                    a.cnt[(int64_t)t * a.n_b + b] = total;
+                    if (kept)
+                        atomicAdd(&s_stored, kept);
+                    if (total > cap)
+                        atomicOr(&s_ovf, 1);
+                }
             }
-            const int kept = total < cap ? total : cap;
-            for (int s = kept + lane; s < cap; s += 64) {
-                store_elem(a.val + slot0 + s, 0.f);
-                a.idx[slot0 + s] = 0;
-            }
-            if (lane == 0)
-                a.cnt[(int64_t)t * a.n_b + b] = total;
         }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a.row_ovf[t] = s_ovf;
+        a.work[t] = s_ovf ? 0 : s_stored;
     }
 }
 
@@ -95,46 +154,66 @@ __global__ __launch_bounds__(256) void relu_rows_kernel(const TI *h, int F, cons
     const int nv = *n_ovf < max_ovf ? *n_ovf : max_ovf;
     if (i >= nv)
         return;
-    const TI *src = h + (int64_t)ovf_rows[i] * F;
-    TI *dst = dense + (int64_t)i * F;
-    for (int j = threadIdx.x; j < F; j += 256) {
-        const float v = load_elem(src + j);
-        store_elem(dst + j, v > 0.f ? v : 0.f);
+    constexpr int CPL = 16 / (int)sizeof(TI);
+    const char *src = reinterpret_cast<const char *>(h + (int64_t)ovf_rows[i] * F);
+    char *dst = reinterpret_cast<char *>(dense + (int64_t)i * F);
+    for (int c = threadIdx.x; c < F / CPL; c += 256) {
+        const u32x4 v = ldg16(src + (int64_t)c * 16);
+        u32x4 o = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            if (chunk_elem<TI>(v, e) > 0.f) {  // keep the element's bits; 0, negatives and NaN -> +0
+                if constexpr (sizeof(TI) == 2)
+                    o[e >> 1] |= v[e >> 1] & ((e & 1) ? 0xFFFF0000u : 0x0000FFFFu);
+                else
+                    o[e] = v[e];
+            }
+        }
+        *reinterpret_cast<u32x4 *>(dst + (int64_t)c * 16) = o;
     }
 }
 
-// Row t of the dense matrix from its TwELL tiles (kept slots only).
+// Row t of the dense matrix from its TwELL tiles (kept slots only).  A wave
+// pass covers 64 * CPL columns (whole tiles): the pass is zeroed in a per-wave
+// LDS row, the tiles' kept slots are scattered into it by column, and each
+// lane writes its CPL columns with one 16-byte store.
 template <typename TI>
 __global__ __launch_bounds__(512) void twell_expand_kernel(ConvArgs<TI> a)
 {
-    constexpr int NW = 8;
-    __shared__ float srow[NW][256];
+    constexpr int NW = 8, CPL = 16 / (int)sizeof(TI), PW = 64 * CPL;  // columns per wave pass
+    __shared__ __attribute__((aligned(16))) TI srow[NW][PW];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = blockIdx.x;
     const int w = a.tile_w, cap = a.cap;
-    float *sr = srow[wave];
-    TI *orow = a.dense + (int64_t)t * a.F;
-    for (int b = wave; b < a.n_b; b += NW) {
-        const int64_t slot0 = ((int64_t)t * a.n_b + b) * cap;
-        int kept = a.cnt[(int64_t)t * a.n_b + b];
-        kept = kept < cap ? kept : cap;
-        kept = kept > 0 ? kept : 0;
-        for (int c = lane; c < w; c += 64)
-            sr[c] = 0.f;
+    TI *sr = srow[wave];
+    char *orow = reinterpret_cast<char *>(a.dense + (int64_t)t * a.F);
+    const int F16 = a.F / CPL;
+    for (int p = wave; p * 64 < F16; p += NW) {
+        const int c0 = p * PW;                                // first column of the pass
+        const int ncol = a.F - c0 < PW ? a.F - c0 : PW;       // multiple of w
+        const int nt = ncol / w, b0 = c0 / w;
+        *reinterpret_cast<u32x4 *>(sr + lane * CPL) = u32x4{0, 0, 0, 0};
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
-        for (int s = lane; s < kept; s += 64) {
-            const int c = a.idx[slot0 + s];
-            if (c < w)  // memory safety for a corrupt index
-                sr[c] = load_elem(a.val + slot0 + s);
+        for (int i = lane; i < nt * cap; i += 64) {
+            const int tl = i / cap, sl = i - tl * cap;
+            const int64_t tb = (int64_t)t * a.n_b + b0 + tl;
+            int kept = a.cnt[tb];
+            kept = kept < cap ? kept : cap;
+            if (sl < kept) {
+                const int c = a.idx[tb * cap + sl];
+                if (c < w)  // memory safety for a corrupt index
+                    sr[tl * w + c] = a.val[tb * cap + sl];
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_wave_barrier();
-        for (int c = lane; c < w; c += 64)
-            store_elem(orow + (int64_t)b * w + c, sr[c]);
+        const int ch = p * 64 + lane;
+        if (ch < F16)
+            *reinterpret_cast<u32x4 *>(orow + (int64_t)ch * 16) = *reinterpret_cast<const u32x4 *>(sr + lane * CPL);
         __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();  // LDS reads done before the next tile's zeros
+        __builtin_amdgcn_wave_barrier();  // LDS reads done before the next pass's zeros
     }
 }
 
@@ -160,12 +239,10 @@ static hipError_t dense_to_hybrid_go(const void *h, int T, int F, int tile_w, in
                                      int32_t *order, int max_ovf, void *dense, hipStream_t s)
 {
     ConvArgs<TI> a{const_cast<TI *>(static_cast<const TI *>(h)), T, F, tile_w, cap, F / tile_w,
-                   static_cast<TI *>(val), idx, cnt};
+                   static_cast<TI *>(val), idx, cnt, row_ovf, order};
     dense_pack_kernel<TI><<<dim3(T), dim3(512), 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
-        return e;
-    if ((e = launch_row_flags(cnt, T, F / tile_w, cap, row_ovf, order, s)) != hipSuccess)
         return e;
     if ((e = launch_compact_rows(row_ovf, T, max_ovf, ovf_rows, n_ovf, order, s)) != hipSuccess)
         return e;
@@ -193,7 +270,7 @@ static hipError_t hybrid_to_dense_go(const int32_t *cnt, const void *val, const 
 {
     ConvArgs<TI> a{static_cast<TI *>(out), T, F, tile_w, cap, F / tile_w,
                    const_cast<TI *>(static_cast<const TI *>(val)), const_cast<uint8_t *>(idx),
-                   const_cast<int32_t *>(cnt)};
+                   const_cast<int32_t *>(cnt), nullptr, nullptr};
     twell_expand_kernel<TI><<<dim3(T), dim3(512), 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || max_ovf == 0)
