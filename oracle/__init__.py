@@ -21,6 +21,8 @@ Models", gist.science summary page):
   * x.W_u) . W_d, accumulated over neurons in ascending order in fp64.
 * ``gate_stats``: section 2.4's L1 activation penalty and dead neurons, as
   per-neuron active counts and per (row, tile) sums of the active gate values.
+* ``compact_hybrid`` / ``compact_to_dense``: section 2.3's compact storage of
+  the hybrid (reading: exact entries per fitting row, dense overflow rows).
 * ``hybrid_to_dense``: section 2.4's hybrid-to-dense conversion; the
   dense-to-hybrid direction is ``pack_twell`` + ``partition_overflow`` +
   ``dense_backup`` applied to a dense activation matrix.
@@ -31,8 +33,9 @@ patterns of one 8-wide tile, a hand-worked example (tests/golden), closed forms
 bitwise, nonzero conservation, round trip, numpy fp64 matmul cross-check,
 bf16 rounding against torch's conversion, for ``gate_stats`` brute force,
 conservation against the TwELL counts and closed forms (all dead, all active,
-one live neuron), and for ``hybrid_to_dense`` the exact round trip through the
-dense-to-hybrid direction and a hand-built example.
+one live neuron), for ``hybrid_to_dense`` the exact round trip through the
+dense-to-hybrid direction and a hand-built example, and for ``compact_hybrid``
+the hand example, the exact round trip and nonzero conservation.
 """
 
 from __future__ import annotations
@@ -182,6 +185,42 @@ def hybrid_to_dense(tw: TwELL, ovf_rows, dense, max_ovf: int) -> np.ndarray:
     out = unpack_twell(tw)
     for i, t in enumerate(np.asarray(ovf_rows)[:max_ovf]):
         out[int(t)] = np.asarray(dense[i], np.float64)
+    return out
+
+
+def compact_hybrid(tw: TwELL, row_ovf, ovf_rows, dense, max_ovf: int) -> dict:
+    """Compacted hybrid storage (section 2.3: the sparse part stored compactly,
+    the dense part sized by the rows that need it), in the reading of this
+    library: the rows that fit keep exactly their entries, row by row in
+    ascending column order (row_ptr [T+1], global column, value: no slot
+    padding), overflow rows keep none there; the overflow rows are listed in
+    ascending order with their dense rows (the first max_ovf of them held)."""
+    T = tw.T
+    row_ptr = np.zeros(T + 1, np.int64)
+    cols, vals = [], []
+    kept = tw.kept()
+    for t in range(T):
+        if not row_ovf[t]:
+            b, sl = np.nonzero(kept[t])
+            c = b * tw.tile_w + tw.idx[t, b, sl].astype(np.int64)
+            cols.extend(c.tolist())
+            vals.extend(tw.val[t, b, sl].tolist())
+        row_ptr[t + 1] = len(cols)
+    n = len(ovf_rows)
+    m = min(n, max_ovf)
+    return {"row_ptr": row_ptr, "col": np.asarray(cols, np.int64), "val": np.asarray(vals, np.float64),
+            "ovf_rows": np.asarray(ovf_rows, np.int64), "n_ovf": n,
+            "dense": np.asarray(dense, np.float64)[:m], "complete": m == n}
+
+
+def compact_to_dense(c: dict, T: int, F: int) -> np.ndarray:
+    """[T][F] from the compacted storage (zeros where nothing is held)."""
+    out = np.zeros((T, F), np.float64)
+    for t in range(T):
+        a, b = c["row_ptr"][t], c["row_ptr"][t + 1]
+        out[t, c["col"][a:b]] = c["val"][a:b]
+    for i in range(len(c["dense"])):
+        out[c["ovf_rows"][i]] = c["dense"][i]
     return out
 
 

@@ -321,3 +321,41 @@ def test_dense_hybrid_round_trip(w, cap):
     out = oracle.hybrid_to_dense(tw, rows, dense, max_ovf=n)
     want = np.where(h > 0, h, 0.0)
     np.testing.assert_array_equal(out, want)
+
+
+def test_compact_hybrid_hand_example():
+    """Same matrix as the hybrid-to-dense example: row 0 fits (entries at
+    columns 1, 3, 7), rows 1 and 2 overflow; max_ovf = 1 holds row 1 densely."""
+    h = np.array([[0.0, 1.5, 0.0, 2.0, 0.0, 0.0, 0.0, 3.0],
+                  [4.0, 5.0, 6.0, 0.0, 0.0, 0.0, 7.0, 0.0],
+                  [0.0, 1.0, 1.0, 1.0, 0.0, 0.0, 0.0, 0.0]])
+    tw = oracle.pack_twell(h, 4, 2, "f32")
+    row_ovf, rows, n = oracle.partition_overflow(tw.cnt, 2)
+    c = oracle.compact_hybrid(tw, row_ovf, rows, oracle.dense_backup(h, rows, "f32"), max_ovf=1)
+    assert list(c["row_ptr"]) == [0, 3, 3, 3]
+    assert list(c["col"]) == [1, 3, 7] and list(c["val"]) == [1.5, 2.0, 3.0]
+    assert list(c["ovf_rows"]) == [1, 2] and c["n_ovf"] == 2 and not c["complete"]
+    np.testing.assert_array_equal(c["dense"], h[1:2])
+    out = oracle.compact_to_dense(c, 3, 8)
+    np.testing.assert_array_equal(out[:2], h[:2])
+    assert not out[2].any()  # row 2 is held nowhere
+
+
+@pytest.mark.parametrize("w,cap", [(32, 2), (256, 16)])
+def test_compact_round_trip_and_conservation(w, cap):
+    rng = np.random.default_rng(7 * w + cap)
+    T, F = 60, 512
+    h = rng.standard_normal((T, F)) * (rng.random((T, F)) < 0.06)
+    h[4, :300] = np.abs(h[4, :300]) + 1.0
+    h = oracle.store_round(h, "bf16")
+    tw = oracle.pack_twell(h, w, cap, "bf16")
+    row_ovf, rows, n = oracle.partition_overflow(tw.cnt, cap)
+    c = oracle.compact_hybrid(tw, row_ovf, rows, oracle.dense_backup(h, rows, "bf16"), max_ovf=n)
+    assert c["complete"]
+    np.testing.assert_array_equal(oracle.compact_to_dense(c, T, F), np.where(h > 0, h, 0.0))
+    # entries held compactly = positives of the rows that fit
+    fit = row_ovf == 0
+    assert c["row_ptr"][-1] == int((h[fit] > 0).sum())
+    for t in range(T):
+        cs = c["col"][c["row_ptr"][t]:c["row_ptr"][t + 1]]
+        assert (np.diff(cs) > 0).all()
