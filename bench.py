@@ -349,8 +349,30 @@ def main():
             conv[name] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes,
                           "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        # compacted storage of the layer's hybrid (the activations training would save)
+        cbuf = torch.empty(int(out["memory"]["twell_bytes"] + out["memory"]["dense_backup_bytes"] + (1 << 20)),
+                           dtype=torch.uint8, device=dev)
+        tw.twell_compact_hybrid(hy, cbuf)
+        hdr = tw.compact_header(cbuf)
+        if hdr["fits"]:
+            for name, fn, nbytes in (("compact", lambda: tw.twell_compact_hybrid(hy, cbuf), side + hdr["bytes"]),
+                                     ("compact_to_dense",
+                                      lambda: tw.twell_compact_to_dense(cbuf, wl.T, wl.F, dt, dense_h),
+                                      wl.T * wl.F * esz + hdr["bytes"])):
+                evc = [(DevEvent(), DevEvent()) for _ in range(args.steps)]
+                for e in evc:
+                    e[0].record()
+                    fn()
+                    e[1].record()
+                torch.cuda.synchronize()
+                ms = float(np.mean([a.elapsed_time(b) for a, b in evc]))
+                conv[name] = {"ms": round(ms, 4), "algorithmic_bytes": int(nbytes),
+                              "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        out["memory"]["compact_bytes"] = int(hdr["bytes"])
+        out["memory"]["compact_vs_dense_h"] = round(hdr["bytes"] / out["memory"]["dense_h_bytes"], 4)
         out["conversions"] = conv
-        del dense_h, hc
+        del dense_h, hc, cbuf
 
     # ---- cold-cache variant: flush MALL/L2 with a 1 GiB write between steps (outside the events)
     if not args.no_cold:

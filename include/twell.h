@@ -194,6 +194,49 @@ TWELL_API int twell_dense_to_hybrid(const void *h, const twell_hybrid_t *hy, voi
  * twell_pack_gate_hybrid or twell_ffn_decode. */
 TWELL_API int twell_hybrid_to_dense(const twell_hybrid_t *hy, void *out, void *stream);
 
+/* Compacted hybrid storage (section 2.3 of the page: the rows with few
+ * nonzeros kept in a compact sparse part, the overflow rows densely, memory
+ * sized by what the rows need).  TwELL pads every tile to cap slots; the
+ * compact form keeps exactly the entries of the rows that fit.  It lives in
+ * one device buffer laid out as
+ *   [0, 256)                  twell_compact_header_t
+ *   off_row_ptr               int32 [T + 1]: row t's entries are [row_ptr[t], row_ptr[t+1])
+ *   off_col                   uint16 [n_entries]: global column, ascending within a row
+ *   off_val                   vdtype [n_entries]
+ *   off_ovf                   int32 [n_dense]: ids of the overflow rows held densely
+ *   off_dense                 vdtype [n_dense][F]
+ * (sections 256-byte aligned).  Overflow rows have no compact entries; the
+ * first n_dense = min(n_ovf, max_ovf) of them are held densely.  The layout
+ * depends on counts only the device knows, so the header is written on the
+ * device: read it after the call to learn `bytes`. */
+typedef struct twell_compact_header_t {
+    int32_t T, F, tile_w, vdtype;
+    int32_t n_entries;  /* entries of the rows that fit */
+    int32_t n_ovf;      /* overflow rows */
+    int32_t n_dense;    /* overflow rows held densely = min(n_ovf, max_ovf) */
+    int32_t fits;       /* 1: the buffer held everything; 0: only the header and row_ptr were written */
+    int64_t off_row_ptr, off_col, off_val, off_ovf, off_dense;
+    int64_t bytes;      /* bytes the compact form needs */
+} twell_compact_header_t;
+
+/* Bytes every compact buffer needs before its variable part: the header and
+ * the row offsets (written even when the rest does not fit). */
+TWELL_API size_t twell_compact_min_bytes(int32_t T);
+
+/* Write the compact form of a hybrid (as written by twell_pack_gate_hybrid,
+ * twell_dense_to_hybrid or twell_ffn_decode) into buf (device, 256-byte
+ * aligned, buf_bytes >= twell_compact_min_bytes(T)).  When buf_bytes is
+ * smaller than the header's `bytes`, fits = 0 and only the header and the row
+ * offsets are written: call again with a buffer of `bytes`.  Requires
+ * F <= 65536 and F / tile_w <= 512. */
+TWELL_API int twell_compact_hybrid(const twell_hybrid_t *hy, void *buf, size_t buf_bytes, void *stream);
+
+/* Dense activations from a compact buffer: out : device [T][F] vdtype,
+ * 16-byte aligned, every element written (zeros where nothing is held; all
+ * zeros when the header says fits = 0 or its T, F differ from the
+ * arguments). */
+TWELL_API int twell_compact_to_dense(const void *buf, int32_t T, int32_t F, int32_t vdtype, void *out, void *stream);
+
 /* Bytes of device workspace twell_ffn_decode needs for these sizes (0 when
  * the sizes are outside its range). */
 TWELL_API size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t tile_w);

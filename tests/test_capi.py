@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 103
+    assert lib.twell_version() == 104
 
 
 def test_status_strings():
@@ -144,6 +144,29 @@ def test_conversion_validation():
     empty = tw.TwellHybridT(_desc(T=0), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
     assert lib.twell_hybrid_to_dense(ctypes.byref(empty), None, None) == 0
     assert lib.twell_dense_to_hybrid(None, ctypes.byref(empty), None) == 0
+
+
+def test_compact_validation():
+    import struct
+    lib = tw.load()
+    # the binding's header description matches the C struct's size
+    assert struct.calcsize("<" + "".join(f for _, f in tw.COMPACT_HEADER)) == 80
+    assert lib.twell_compact_min_bytes(16) == 256 + 256
+    assert lib.twell_compact_min_bytes(100) == 256 + 512
+    hy = tw.TwellHybridT(_desc(), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
+    need = lib.twell_compact_min_bytes(16)
+    assert lib.twell_compact_hybrid(None, GOOD, need, None) == -1
+    assert lib.twell_compact_hybrid(ctypes.byref(hy), None, need, None) == -1
+    assert lib.twell_compact_hybrid(ctypes.byref(hy), GOOD + 16, need, None) == -2
+    assert lib.twell_compact_hybrid(ctypes.byref(hy), GOOD, need - 1, None) == -6
+    big = tw.TwellHybridT(_desc(F=131072, w=256), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
+    assert lib.twell_compact_hybrid(ctypes.byref(big), GOOD, need, None) == -4   # F > 65536
+    assert lib.twell_compact_to_dense(GOOD, 16, 512, 2, GOOD, None) == -4      # dtype
+    assert lib.twell_compact_to_dense(GOOD, 16, 500, 1, GOOD, None) == -3      # F % 64
+    assert lib.twell_compact_to_dense(None, 16, 512, 1, GOOD, None) == -1
+    assert lib.twell_compact_to_dense(GOOD + 64, 16, 512, 1, GOOD, None) == -2
+    assert lib.twell_compact_to_dense(GOOD, 16, 512, 1, GOOD + 2, None) == -2
+    assert lib.twell_compact_to_dense(None, 0, 512, 1, None, None) == 0
 
 
 def test_binding_requires_library(tmp_path, monkeypatch):

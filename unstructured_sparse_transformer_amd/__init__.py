@@ -10,7 +10,8 @@ The functions carry the C names (``include/twell.h``):
 ``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
 ``twell_ffn_hybrid_workspace_bytes``, ``twell_ffn_decode``,
 ``twell_ffn_decode_workspace_bytes``, ``twell_dense_to_hybrid``,
-``twell_hybrid_to_dense``.
+``twell_hybrid_to_dense``, ``twell_compact_min_bytes``, ``twell_compact_hybrid``,
+``twell_compact_to_dense``.
 """
 
 from __future__ import annotations
@@ -28,7 +29,8 @@ STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_S
 EXPORTS = ("twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
            "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
            "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_dense_to_hybrid", "twell_hybrid_to_dense",
-           "twell_status_str", "twell_version")
+           "twell_compact_min_bytes", "twell_compact_hybrid", "twell_compact_to_dense", "twell_status_str",
+           "twell_version")
 
 
 class TwellT(ctypes.Structure):
@@ -77,12 +79,17 @@ def load(path: str = LIB_PATH):
     lib.twell_ffn_decode.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P, ctypes.c_size_t, P]
     lib.twell_dense_to_hybrid.argtypes = [P, ctypes.POINTER(TwellHybridT), P]
     lib.twell_hybrid_to_dense.argtypes = [ctypes.POINTER(TwellHybridT), P, P]
+    lib.twell_compact_min_bytes.argtypes = [I32]
+    lib.twell_compact_min_bytes.restype = ctypes.c_size_t
+    lib.twell_compact_hybrid.argtypes = [ctypes.POINTER(TwellHybridT), P, ctypes.c_size_t, P]
+    lib.twell_compact_to_dense.argtypes = [P, I32, I32, I32, P, P]
     lib.twell_status_str.argtypes = [ctypes.c_int]
     lib.twell_status_str.restype = ctypes.c_char_p
     lib.twell_version.restype = ctypes.c_int
     for fn in (lib.twell_pack_gate, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
                lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_decode,
-               lib.twell_dense_to_hybrid, lib.twell_hybrid_to_dense):
+               lib.twell_dense_to_hybrid, lib.twell_hybrid_to_dense, lib.twell_compact_hybrid,
+               lib.twell_compact_to_dense):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -233,6 +240,34 @@ def twell_dense_to_hybrid(h, hy: Hybrid, stream=None):
 def twell_hybrid_to_dense(hy: Hybrid, out, stream=None):
     """out: [T][F] in the hybrid's value dtype (every element written)."""
     _check("twell_hybrid_to_dense", load().twell_hybrid_to_dense(ctypes.byref(hy.desc()), _ptr(out), _stream(stream)))
+
+
+COMPACT_HEADER = (("T", "i"), ("F", "i"), ("tile_w", "i"), ("vdtype", "i"), ("n_entries", "i"), ("n_ovf", "i"),
+                  ("n_dense", "i"), ("fits", "i"), ("off_row_ptr", "q"), ("off_col", "q"), ("off_val", "q"),
+                  ("off_ovf", "q"), ("off_dense", "q"), ("bytes", "q"))
+
+
+def twell_compact_min_bytes(T: int) -> int:
+    return int(load().twell_compact_min_bytes(T))
+
+
+def twell_compact_hybrid(hy: Hybrid, buf, stream=None):
+    """buf: a uint8 device tensor (256-byte aligned by the allocator)."""
+    _check("twell_compact_hybrid", load().twell_compact_hybrid(ctypes.byref(hy.desc()), _ptr(buf),
+                                                               buf.numel() * buf.element_size(), _stream(stream)))
+
+
+def twell_compact_to_dense(buf, T: int, F: int, dtype, out, stream=None):
+    _check("twell_compact_to_dense", load().twell_compact_to_dense(_ptr(buf), T, F, vdtype_of(dtype), _ptr(out),
+                                                                   _stream(stream)))
+
+
+def compact_header(buf) -> dict:
+    """The header of a compact buffer, read back to the host (synchronises)."""
+    import struct
+    fmt = "<" + "".join(f for _, f in COMPACT_HEADER)
+    raw = bytes(buf[: struct.calcsize(fmt)].cpu().numpy().tobytes())
+    return dict(zip((n for n, _ in COMPACT_HEADER), struct.unpack(fmt, raw)))
 
 
 def twell_ffn_decode_workspace_bytes(T: int, F: int, d: int, tile_w: int) -> int:

@@ -97,7 +97,7 @@ size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
 
 extern "C" {
 
-int twell_version(void) { return 103; }
+int twell_version(void) { return 104; }
 
 const char *twell_status_str(int status)
 {
@@ -213,6 +213,52 @@ int twell_hybrid_to_dense(const twell_hybrid_t *hy, void *out, void *stream)
     return hip_status(twell::launch_hybrid_to_dense(e->vdtype, e->cnt, e->val, e->idx, e->T, e->F, e->tile_w, e->cap,
                                                     hy->ovf_rows, hy->n_ovf, hy->max_ovf, hy->dense, out,
                                                     static_cast<hipStream_t>(stream)));
+}
+
+static_assert(sizeof(twell_compact_header_t) == 80, "compact header layout");
+
+size_t twell_compact_min_bytes(int32_t T)
+{
+    if (T < 0)
+        return 0;
+    return 256 + (((size_t)(T + 1) * 4 + 255) & ~(size_t)255);
+}
+
+int twell_compact_hybrid(const twell_hybrid_t *hy, void *buf, size_t buf_bytes, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *e = &hy->ell;
+    TWELL_TRY(check_layout(e, 64));
+    TWELL_TRY(check_hybrid(hy));
+    if (e->F > 65536 || e->F / e->tile_w > twell::DEC_MAX_NB)
+        return TWELL_E_UNSUPPORTED;
+    if (!buf)
+        return TWELL_E_NULL;
+    if (reinterpret_cast<uintptr_t>(buf) & 255u)
+        return TWELL_E_ALIGN;
+    if (buf_bytes < twell_compact_min_bytes(e->T))
+        return TWELL_E_WORKSPACE;
+    if (e->T > 0)
+        TWELL_TRY(check_ptrs(e));
+    return hip_status(twell::launch_compact_hybrid(e->vdtype, e->cnt, e->val, e->idx, hy->row_ovf, hy->ovf_rows,
+                                                   hy->n_ovf, hy->max_ovf, hy->dense, e->T, e->F, e->tile_w, e->cap,
+                                                   buf, (int64_t)buf_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int twell_compact_to_dense(const void *buf, int32_t T, int32_t F, int32_t vdtype, void *out, void *stream)
+{
+    if (vdtype != TWELL_F32 && vdtype != TWELL_BF16)
+        return TWELL_E_UNSUPPORTED;
+    if (T < 0 || F <= 0 || F % 64 != 0)
+        return TWELL_E_SHAPE;
+    if (T == 0)
+        return TWELL_OK;
+    if (!buf || !out)
+        return TWELL_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(buf) & 255u) || !aligned16(out))
+        return TWELL_E_ALIGN;
+    return hip_status(twell::launch_compact_to_dense(vdtype, buf, T, F, out, static_cast<hipStream_t>(stream)));
 }
 
 size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t tile_w)

@@ -75,6 +75,15 @@ hipError_t launch_hybrid_to_dense(int vdtype, const int32_t *cnt, const void *va
                                   int tile_w, int cap, const int32_t *ovf_rows, const int32_t *n_ovf, int max_ovf,
                                   const void *dense, void *out, hipStream_t s);
 
+// Compact form of the hybrid into buf (layout and header as in twell.h).
+hipError_t launch_compact_hybrid(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx,
+                                 const int32_t *row_ovf, const int32_t *ovf_rows, const int32_t *n_ovf, int max_ovf,
+                                 const void *dense, int T, int F, int tile_w, int cap, void *buf, int64_t buf_bytes,
+                                 hipStream_t s);
+
+// Dense [T][F] from a compact buffer.
+hipError_t launch_compact_to_dense(int vdtype, const void *buf, int T, int F, void *out, hipStream_t s);
+
 // Number of split-K slabs the hybrid down projection uses for these sizes.
 int down_splits(int max_ovf, int F, int d);
 
