@@ -21,6 +21,8 @@ Models", gist.science summary page):
   * x.W_u) . W_d, accumulated over neurons in ascending order in fp64.
 * ``gate_stats``: section 2.4's L1 activation penalty and dead neurons, as
   per-neuron active counts and per (row, tile) sums of the active gate values.
+* ``ffn_backward``: the gradients of the FFN (section 2.4's training
+  kernels), per active (row, neuron) in ascending order.
 * ``compact_hybrid`` / ``compact_to_dense``: section 2.3's compact storage of
   the hybrid (reading: exact entries per fitting row, dense overflow rows).
 * ``hybrid_to_dense``: section 2.4's hybrid-to-dense conversion; the
@@ -35,7 +37,9 @@ bf16 rounding against torch's conversion, for ``gate_stats`` brute force,
 conservation against the TwELL counts and closed forms (all dead, all active,
 one live neuron), for ``hybrid_to_dense`` the exact round trip through the
 dense-to-hybrid direction and a hand-built example, and for ``compact_hybrid``
-the hand example, the exact round trip and nonzero conservation.
+the hand example, the exact round trip and nonzero conservation, and for
+``ffn_backward`` central finite differences of an independent numpy forward,
+the matrix form with numpy matmuls, and a one-neuron closed form.
 """
 
 from __future__ import annotations
@@ -70,6 +74,7 @@ def _load():
     lib.orc_partition.restype = I
     lib.orc_ffn_dense.argtypes = [P, P, P, I, I, I, I, P]
     lib.orc_gate_stats.argtypes = [P, I, I, I, P, P]
+    lib.orc_ffn_backward.argtypes = [P, I, I, P, P, P, P, I, I, P, P, P, P, P]
     lib.orc_ffn_twell.argtypes = [P, P, P, I, I, I, I, P, P, P, I, I, P]
     lib.orc_ffn_active.argtypes = [P, I, I, P, P, P, I, I, P]
     _lib = lib
@@ -278,6 +283,27 @@ def ffn_active(z: np.ndarray, x, wu_t, wd, hround=None) -> np.ndarray:
     y = np.empty((T, d), np.float64)
     lib.orc_ffn_active(_p(z), T, F, _p(x), _p(wu_t), _p(wd), d, _vd(hround), _p(y))
     return y
+
+
+def ffn_backward(z: np.ndarray, x, wg_t, wu_t, wd, dy, hround=None):
+    """Gradients (dx [T][d], dW_g^T, dW_u^T, dW_d [F][d], all fp64) of
+    sum(y * dy) for the FFN of ``ffn_active``: section 2.4's backward pass,
+    with the stored gate value h in the products and ReLU's derivative 1 on
+    the active neurons (scalar C loops, ascending rows and neurons)."""
+    lib = _load()
+    z = _c(z, np.float64)
+    x = _c(x, np.float32)
+    wg_t, wu_t, wd = _c(wg_t, np.float32), _c(wu_t, np.float32), _c(wd, np.float32)
+    dy = _c(dy, np.float64)
+    T, F = z.shape
+    d = x.shape[1]
+    dx = np.empty((T, d), np.float64)
+    dwg = np.empty((F, d), np.float64)
+    dwu = np.empty((F, d), np.float64)
+    dwd = np.empty((F, d), np.float64)
+    lib.orc_ffn_backward(_p(z), T, F, _p(x), _p(wg_t), _p(wu_t), _p(wd), d, _vd(hround), _p(dy), _p(dx), _p(dwg),
+                         _p(dwu), _p(dwd))
+    return dx, dwg, dwu, dwd
 
 
 def ffn_numpy(x, wg_t, wu_t, wd) -> np.ndarray:

@@ -256,3 +256,46 @@ EXPORT void orc_gate_stats(const double *z, int T, int F, int w, int64_t *neuron
         }
     }
 }
+
+/* Backward of the FFN above (the page's training kernels, section 2.4, need
+ * the gradients of y = sum over active j of h_j (x.W_u^T[j]) W_d[j]).  With
+ * dy [T][d] given, per row t and active neuron j (z > 0, ascending j), h the
+ * stored gate value (ReLU(z) rounded as hround says, derivative 1 where active):
+ *   u = x_t . W_u^T[j],  g = dy_t . W_d[j],  du = g h,  dz = g u,
+ *   dx_t += du W_u^T[j] + dz W_g^T[j],  dW_d[j] += (h u) dy_t,
+ *   dW_u^T[j] += du x_t,  dW_g^T[j] += dz x_t.
+ * All outputs fp64 and overwritten; rows (t) and neurons (j) in ascending order. */
+EXPORT void orc_ffn_backward(const double *z, int T, int F, const float *x, const float *wg_t, const float *wu_t,
+                             const float *wd, int d, int hround, const double *dy, double *dx, double *dwg,
+                             double *dwu, double *dwd)
+{
+    for (int64_t i = 0; i < (int64_t)T * d; ++i)
+        dx[i] = 0.0;
+    for (int64_t i = 0; i < (int64_t)F * d; ++i)
+        dwg[i] = dwu[i] = dwd[i] = 0.0;
+    for (int t = 0; t < T; ++t) {
+        const float *xt = x + (int64_t)t * d;
+        const double *dyt = dy + (int64_t)t * d;
+        double *dxt = dx + (int64_t)t * d;
+        for (int j = 0; j < F; ++j) {
+            const double zz = z[(int64_t)t * F + j];
+            if (!(zz > 0.0))
+                continue;
+            const double h = orc_store(zz, hround);
+            const float *wuj = wu_t + (int64_t)j * d;
+            const float *wgj = wg_t + (int64_t)j * d;
+            const float *wdj = wd + (int64_t)j * d;
+            const double u = orc_dot(xt, wuj, d);
+            double g = 0.0;
+            for (int k = 0; k < d; ++k)
+                g += dyt[k] * (double)wdj[k];
+            const double du = g * h, dz = g * u, hu = h * u;
+            for (int k = 0; k < d; ++k) {
+                dxt[k] += du * (double)wuj[k] + dz * (double)wgj[k];
+                dwd[(int64_t)j * d + k] += hu * dyt[k];
+                dwu[(int64_t)j * d + k] += du * (double)xt[k];
+                dwg[(int64_t)j * d + k] += dz * (double)xt[k];
+            }
+        }
+    }
+}

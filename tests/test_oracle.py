@@ -359,3 +359,93 @@ def test_compact_round_trip_and_conservation(w, cap):
     for t in range(T):
         cs = c["col"][c["row_ptr"][t]:c["row_ptr"][t + 1]]
         assert (np.diff(cs) > 0).all()
+
+
+# ------------------------------------------------------------ backward pass
+def _np_forward(x, wg_t, wu_t, wd):
+    """An independent fp64 forward for finite differences: ReLU(x W_g) * (x W_u), then W_d."""
+    z = x @ wg_t.T
+    return (np.where(z > 0, z, 0.0) * (x @ wu_t.T)) @ wd
+
+
+def _small_problem(seed):
+    rng = np.random.default_rng(seed)
+    T, d, F = 3, 8, 16
+    x = _f32(rng.integers(-4, 5, (T, d)) / 4)
+    wg = _f32(rng.integers(-4, 5, (F, d)) / 8)
+    wu = _f32(rng.integers(-4, 5, (F, d)) / 8)
+    wd = _f32(rng.integers(-4, 5, (F, d)) / 8)
+    dy = rng.integers(-3, 4, (T, d)) / 2.0
+    # a ones column and a 1/64 bias keep every z off 0 (other terms are multiples of 1/32)
+    x[:, -1] = 1.0
+    wg[:, -1] = _f32(np.full(F, 1 / 64) + rng.integers(-2, 3, F) / 8)
+    return x, wg, wu, wd, dy
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_backward_finite_differences(seed):
+    """Every gradient entry against central differences of sum(y * dy) of an
+    independent numpy forward (fp64, h = ReLU(z) unrounded); the active set
+    does not change for the step used (|z| is far from 0 on the grid)."""
+    x, wg, wu, wd, dy = _small_problem(seed)
+    z = x.astype(np.float64) @ wg.astype(np.float64).T
+    assert np.min(np.abs(z)) >= 1.0 / 64  # grid values: no sign change within eps
+    dx, dwg, dwu, dwd = oracle.ffn_backward(z, x, wg, wu, wd, dy, None)
+    base = [a.astype(np.float64) for a in (x, wg, wu, wd)]
+    loss = lambda p: float((_np_forward(*p) * dy).sum())  # noqa: E731
+    eps = 1e-4
+    for which, grad in ((0, dx), (1, dwg), (2, dwu), (3, dwd)):
+        fd = np.zeros_like(grad)
+        for i in np.ndindex(grad.shape):
+            p = [a.copy() for a in base]
+            p[which][i] += eps
+            lp = loss(p)
+            p[which][i] -= 2 * eps
+            lm = loss(p)
+            fd[i] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=f"parameter {which}")
+
+
+def test_backward_matrix_form():
+    """Library cross-check: the same gradients as dense matrix products (numpy
+    fp64 matmuls) on a random layer, with the stored (bf16) h."""
+    wl = make_random_small(T=40, d=64, F=256, tile_w=64, cap=8, active_frac=0.1, seed=12, jitter=0.5)
+    rng = np.random.default_rng(3)
+    dy = rng.standard_normal((wl.T, wl.d))
+    z = oracle.gate(wl.x, wl.wg_t)
+    dx, dwg, dwu, dwd = oracle.ffn_backward(z, wl.x, wl.wg_t, wl.wu_t, wl.wd, dy, "bf16")
+    x = wl.x.astype(np.float64)
+    H = oracle.store_round(np.where(z > 0, z, 0.0), "bf16")
+    U = x @ wl.wu_t.astype(np.float64).T
+    G = dy @ wl.wd.astype(np.float64).T
+    DU, DZ = G * H, G * U * (z > 0)
+    np.testing.assert_allclose(dx, DU @ wl.wu_t.astype(np.float64) + DZ @ wl.wg_t.astype(np.float64), rtol=1e-10,
+                               atol=1e-10)
+    np.testing.assert_allclose(dwd, (H * U).T @ dy, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(dwu, DU.T @ x, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(dwg, DZ.T @ x, rtol=1e-10, atol=1e-10)
+
+
+def test_backward_single_neuron_closed_form():
+    """One active neuron j: dW_d[j] = sum_t (h_t u_t) dy_t, every other
+    neuron's gradients 0, dx_t = g_t (h_t W_u[j] + u_t W_g[j])."""
+    wl = make_random_small(T=10, d=64, F=128, tile_w=64, cap=4, active_frac=0.5, seed=4)
+    j = 37
+    wl.wg_t[:, -1] = -np.inf
+    wl.wg_t[j, -1] = 2.0
+    z = oracle.gate(wl.x, wl.wg_t)
+    rng = np.random.default_rng(5)
+    dy = rng.standard_normal((wl.T, wl.d))
+    dx, dwg, dwu, dwd = oracle.ffn_backward(z, wl.x, wl.wg_t, wl.wu_t, wl.wd, dy, None)
+    act = z[:, j] > 0
+    assert act.any()
+    others = np.arange(wl.F) != j
+    assert not dwd[others].any() and not dwu[others].any() and not dwg[others].any()
+    x = wl.x.astype(np.float64)
+    u = x @ wl.wu_t[j].astype(np.float64)
+    g = dy @ wl.wd[j].astype(np.float64)
+    h = np.where(act, z[:, j], 0.0)
+    np.testing.assert_allclose(dwd[j], ((h * u)[:, None] * dy).sum(0), rtol=1e-12)
+    want_dx = np.where(act[:, None], g[:, None] * (h[:, None] * wl.wu_t[j].astype(np.float64)
+                                                    + u[:, None] * wl.wg_t[j].astype(np.float64)), 0.0)
+    np.testing.assert_allclose(dx, want_dx, rtol=1e-12, atol=1e-12)
