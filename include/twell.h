@@ -261,6 +261,36 @@ TWELL_API int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t
                                const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Bytes of device workspace twell_ffn_backward needs for these sizes (0 when
+ * they are invalid). */
+TWELL_API size_t twell_ffn_backward_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t max_entries);
+
+/* Backward pass of the sparse FFN on its hybrid (section 2.4 of the page: the
+ * forward and backward passes of training run on the hybrid).  For
+ * y = sum over the active neurons j of row t of h (x[t] . W_u^T[j]) W_d[j],
+ * with h the stored gate value and ReLU's derivative 1 on active entries,
+ * given dy = dL/dy it writes
+ *   dx [T][d], dwg = dL/dW_g^T, dwu = dL/dW_u^T, dwd = dL/dW_d ([F][d]),
+ * all float, overwritten (neurons without entries get zero rows).  The active
+ * entries are a fitting row's TwELL entries and a held overflow row's nonzero
+ * dense-backup values; an overflow row past max_ovf has no dense row and
+ * contributes nothing (its dx row is 0).  Per entry: u = x . W_u^T[j],
+ * g = dy . W_d[j] (fp32), du = g h, dz = g u; every sum in a fixed order, so
+ * repeated calls give the same bits.
+ *   hy : as written by twell_pack_gate_hybrid / twell_dense_to_hybrid /
+ *        twell_ffn_decode, vdtype TWELL_BF16, d <= 2048, F / tile_w <= 512;
+ *   x, wg_t, wu_t, wd : the forward's inputs (bf16); dy : device [T][d] float;
+ *   max_entries : bound on the active entries the workspace holds;
+ *   workspace : >= twell_ffn_backward_workspace_bytes(T, F, d, max_entries),
+ *               256-byte aligned.  Its first 8 bytes hold, after the call,
+ *               int32 entries and int32 too_many: when entries > max_entries
+ *               nothing is computed and every output is zero.
+ * Returns TWELL_OK or a negative twell_status. */
+TWELL_API int twell_ffn_backward(const twell_hybrid_t *hy, const void *x, const void *wg_t, const void *wu_t,
+                                 const void *wd, int32_t d, const float *dy, float *dx, float *dwg, float *dwu,
+                                 float *dwd, int32_t max_entries, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* Static text for a status code. */
 TWELL_API const char *twell_status_str(int status);
 

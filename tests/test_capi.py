@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 104
+    assert lib.twell_version() == 105
 
 
 def test_status_strings():

@@ -11,7 +11,8 @@ The functions carry the C names (``include/twell.h``):
 ``twell_ffn_hybrid_workspace_bytes``, ``twell_ffn_decode``,
 ``twell_ffn_decode_workspace_bytes``, ``twell_dense_to_hybrid``,
 ``twell_hybrid_to_dense``, ``twell_compact_min_bytes``, ``twell_compact_hybrid``,
-``twell_compact_to_dense``.
+``twell_compact_to_dense``, ``twell_ffn_backward``,
+``twell_ffn_backward_workspace_bytes``.
 """
 
 from __future__ import annotations
@@ -29,8 +30,8 @@ STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_S
 EXPORTS = ("twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
            "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
            "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_dense_to_hybrid", "twell_hybrid_to_dense",
-           "twell_compact_min_bytes", "twell_compact_hybrid", "twell_compact_to_dense", "twell_status_str",
-           "twell_version")
+           "twell_compact_min_bytes", "twell_compact_hybrid", "twell_compact_to_dense",
+           "twell_ffn_backward_workspace_bytes", "twell_ffn_backward", "twell_status_str", "twell_version")
 
 
 class TwellT(ctypes.Structure):
@@ -83,13 +84,17 @@ def load(path: str = LIB_PATH):
     lib.twell_compact_min_bytes.restype = ctypes.c_size_t
     lib.twell_compact_hybrid.argtypes = [ctypes.POINTER(TwellHybridT), P, ctypes.c_size_t, P]
     lib.twell_compact_to_dense.argtypes = [P, I32, I32, I32, P, P]
+    lib.twell_ffn_backward_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.twell_ffn_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.twell_ffn_backward.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, P, I32, P, P, P, P, P, I32, P,
+                                       ctypes.c_size_t, P]
     lib.twell_status_str.argtypes = [ctypes.c_int]
     lib.twell_status_str.restype = ctypes.c_char_p
     lib.twell_version.restype = ctypes.c_int
     for fn in (lib.twell_pack_gate, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
                lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_decode,
                lib.twell_dense_to_hybrid, lib.twell_hybrid_to_dense, lib.twell_compact_hybrid,
-               lib.twell_compact_to_dense):
+               lib.twell_compact_to_dense, lib.twell_ffn_backward):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -268,6 +273,31 @@ def compact_header(buf) -> dict:
     fmt = "<" + "".join(f for _, f in COMPACT_HEADER)
     raw = bytes(buf[: struct.calcsize(fmt)].cpu().numpy().tobytes())
     return dict(zip((n for n, _ in COMPACT_HEADER), struct.unpack(fmt, raw)))
+
+
+def twell_ffn_backward_workspace_bytes(T: int, F: int, d: int, max_entries: int) -> int:
+    return int(load().twell_ffn_backward_workspace_bytes(T, F, d, max_entries))
+
+
+def backward_workspace(T: int, F: int, d: int, max_entries: int, device="cuda"):
+    import torch
+    n = twell_ffn_backward_workspace_bytes(T, F, d, max_entries)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def twell_ffn_backward(hy: Hybrid, x, wg_t, wu_t, wd, dy, dx, dwg, dwu, dwd, max_entries: int, workspace,
+                       stream=None):
+    _check("twell_ffn_backward",
+           load().twell_ffn_backward(ctypes.byref(hy.desc()), _ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd),
+                                     int(wg_t.shape[1]), _ptr(dy), _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd),
+                                     max_entries, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+
+
+def backward_status(workspace) -> tuple:
+    """(entries, too_many) from a backward workspace (synchronises)."""
+    v = workspace[:8].cpu().numpy().view("<i4")
+    return int(v[0]), int(v[1])
 
 
 def twell_ffn_decode_workspace_bytes(T: int, F: int, d: int, tile_w: int) -> int:

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtwell.so")
 
-SOURCES = ["capi.cpp", "gate_twell.hip", "ffn_fused.hip", "hybrid.hip", "decode.hip", "convert.hip", "compact.hip"]
+SOURCES = ["capi.cpp", "gate_twell.hip", "ffn_fused.hip", "hybrid.hip", "decode.hip", "convert.hip", "compact.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

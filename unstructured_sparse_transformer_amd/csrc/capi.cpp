@@ -97,7 +97,7 @@ size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
 
 extern "C" {
 
-int twell_version(void) { return 104; }
+int twell_version(void) { return 105; }
 
 const char *twell_status_str(int status)
 {
@@ -259,6 +259,76 @@ int twell_compact_to_dense(const void *buf, int32_t T, int32_t F, int32_t vdtype
     if ((reinterpret_cast<uintptr_t>(buf) & 255u) || !aligned16(out))
         return TWELL_E_ALIGN;
     return hip_status(twell::launch_compact_to_dense(vdtype, buf, T, F, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t twell_ffn_backward_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t max_entries)
+{
+    if (T < 0 || F <= 0 || d <= 0 || max_entries < 0)
+        return 0;
+    return twell::bw_ws_layout(nullptr, T, F, d, max_entries).bytes;
+}
+
+int twell_ffn_backward(const twell_hybrid_t *hy, const void *x, const void *wg_t, const void *wu_t, const void *wd,
+                       int32_t d, const float *dy, float *dx, float *dwg, float *dwu, float *dwd,
+                       int32_t max_entries, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *e = &hy->ell;
+    TWELL_TRY(check_layout(e, d));
+    TWELL_TRY(check_hybrid(hy));
+    if (e->vdtype != TWELL_BF16 || d > twell::BW_MAX_D || e->F / e->tile_w > twell::BW_MAX_NB)
+        return TWELL_E_UNSUPPORTED;
+    if (max_entries < 0)
+        return TWELL_E_SHAPE;
+    TWELL_TRY(check_mat(wg_t));
+    TWELL_TRY(check_mat(wu_t));
+    TWELL_TRY(check_mat(wd));
+    TWELL_TRY(check_mat(dwg));
+    TWELL_TRY(check_mat(dwu));
+    TWELL_TRY(check_mat(dwd));
+    if (!workspace)
+        return TWELL_E_NULL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return TWELL_E_ALIGN;
+    const twell::BwWs w = twell::bw_ws_layout(workspace, e->T, e->F, d, max_entries);
+    if (workspace_bytes < w.bytes)
+        return TWELL_E_WORKSPACE;
+    if (e->T > 0) {
+        TWELL_TRY(check_mat(x));
+        TWELL_TRY(check_mat(dy));
+        TWELL_TRY(check_mat(dx));
+        TWELL_TRY(check_ptrs(e));
+    }
+    twell::BwArgs a{};
+    a.T = e->T;
+    a.F = e->F;
+    a.tile_w = e->tile_w;
+    a.cap = e->cap;
+    a.n_b = e->F / e->tile_w;
+    a.d = d;
+    a.nchunks = d * 2 / 16;
+    a.n_rc = (e->T + twell::BW_RC - 1) / twell::BW_RC;
+    a.max_entries = max_entries;
+    a.max_ovf = hy->max_ovf;
+    a.cnt = e->cnt;
+    a.val = static_cast<const __bf16 *>(e->val);
+    a.idx = e->idx;
+    a.row_ovf = hy->row_ovf;
+    a.ovf_rows = hy->ovf_rows;
+    a.n_ovf = hy->n_ovf;
+    a.dense = static_cast<const __bf16 *>(hy->dense);
+    a.x = static_cast<const __bf16 *>(x);
+    a.wg_t = static_cast<const __bf16 *>(wg_t);
+    a.wu_t = static_cast<const __bf16 *>(wu_t);
+    a.wd = static_cast<const __bf16 *>(wd);
+    a.dy = dy;
+    a.dx = dx;
+    a.dwg = dwg;
+    a.dwu = dwu;
+    a.dwd = dwd;
+    a.ws = w;
+    return hip_status(twell::launch_ffn_backward(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t tile_w)

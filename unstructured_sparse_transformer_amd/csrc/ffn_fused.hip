@@ -560,4 +560,13 @@ hipError_t launch_ffn_decode(const int32_t *cnt, const void *val, const uint8_t 
     return hipGetLastError();
 }
 
+hipError_t launch_chunk_reduce(const float *part, const int32_t *chunk0, int T, int d, float *y, hipStream_t s)
+{
+    if (T == 0)
+        return hipSuccess;
+    chunk_reduce_kernel<<<dim3(T * ((d + 255) / 256)), dim3(256), 0, s>>>(part, chunk0, T, d, y, nullptr, 0, nullptr,
+                                                                          nullptr, 0, nullptr);
+    return hipGetLastError();
+}
+
 }  // namespace twell

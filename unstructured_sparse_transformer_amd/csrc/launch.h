@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "backward.h"
 #include "decode.h"
 
 namespace twell {
@@ -83,6 +84,13 @@ hipError_t launch_compact_hybrid(int vdtype, const int32_t *cnt, const void *val
 
 // Dense [T][F] from a compact buffer.
 hipError_t launch_compact_to_dense(int vdtype, const void *buf, int T, int F, void *out, hipStream_t s);
+
+// y[t] = sum of row t's partial rows part[c] (c in [chunk0[t], chunk0[t+1])),
+// in chunk order.
+hipError_t launch_chunk_reduce(const float *part, const int32_t *chunk0, int T, int d, float *y, hipStream_t s);
+
+// Backward pass of the sparse FFN on the hybrid (arguments in backward.h).
+hipError_t launch_ffn_backward(const BwArgs &a, hipStream_t s);
 
 // Number of split-K slabs the hybrid down projection uses for these sizes.
 int down_splits(int max_ovf, int F, int d);
