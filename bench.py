@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-energy", action="store_true", help="skip the energy-per-token measurement")
     ap.add_argument("--no-stats", action="store_true", help="skip the gate-statistics variant timing")
     ap.add_argument("--no-conversions", action="store_true", help="skip the hybrid <-> dense conversion timing")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--batch-path", action="store_true",
                     help="decode-shaped workloads (T <= 64): time the batch path instead of twell_ffn_decode")
     ap.add_argument("--energy-seconds", type=float, default=2.0, help="run time per energy measurement")
@@ -373,6 +374,48 @@ def main():
         out["memory"]["compact_vs_dense_h"] = round(hdr["bytes"] / out["memory"]["dense_h_bytes"], 4)
         out["conversions"] = conv
         del dense_h, hc, cbuf
+
+    # ---- backward pass on this layer's hybrid, next to the dense bf16 backward
+    # (the same gradients as 2-D torch matmuls on the dense matrices)
+    if not args.no_backward and dt == torch.bfloat16 and wl.d <= 2048:
+        max_e = 1 << 19
+        bws = tw.backward_workspace(wl.T, wl.F, wl.d, max_e)
+        dy = torch.randn((wl.T, wl.d), dtype=torch.float32, device=dev)
+        dxg = torch.empty((wl.T, wl.d), dtype=torch.float32, device=dev)
+        gw = [torch.empty((wl.F, wl.d), dtype=torch.float32, device=dev) for _ in range(3)]
+
+        def sparse_bw():
+            tw.twell_ffn_backward(hy, x, wg, wu, wd, dy, dxg, gw[0], gw[1], gw[2], max_e, bws)
+
+        dyb = dy.to(torch.bfloat16)
+
+        def dense_bw():
+            z = torch.matmul(x, wg.t())
+            u = torch.matmul(x, wu.t())
+            hh = torch.relu(z)
+            g = torch.matmul(dyb, wd.t())
+            du = g * hh
+            dz = g * u * (z > 0)
+            dx_ = torch.matmul(du, wu) + torch.matmul(dz, wg)
+            return dx_, torch.matmul((hh * u).t(), dyb), torch.matmul(du.t(), x), torch.matmul(dz.t(), x)
+
+        bwd = {}
+        for name, fn in (("sparse", sparse_bw), ("dense_bf16", dense_bw)):
+            for _ in range(3):
+                fn()
+            evc = [(DevEvent(), DevEvent()) for _ in range(args.steps)]
+            for e in evc:
+                e[0].record()
+                fn()
+                e[1].record()
+            torch.cuda.synchronize()
+            bwd[name + "_ms"] = round(float(np.mean([a.elapsed_time(b) for a, b in evc])), 4)
+        ent, too_many = tw.backward_status(bws)
+        bwd["entries"] = ent
+        bwd["complete"] = not too_many and n_ovf <= max_ovf
+        bwd["sparse_speedup"] = round(bwd["dense_bf16_ms"] / bwd["sparse_ms"], 3)
+        out["backward"] = bwd
+        del bws, dy, dxg, gw, dyb
 
     # ---- cold-cache variant: flush MALL/L2 with a 1 GiB write between steps (outside the events)
     if not args.no_cold:

@@ -8,7 +8,7 @@
 
 namespace twell {
 
-constexpr int BW_CE = 32;       // entries per token-major chunk
+constexpr int BW_CE = 64;       // entries per token-major chunk
 constexpr int BW_RC = 32;       // rows per block of the neuron regrouping
 constexpr int BW_WGS = 1024;    // workgroups of the grid-stride kernels (4 waves each)
 constexpr int BW_MAX_NB = 512;  // tiles per row held in LDS

@@ -92,10 +92,17 @@ __global__ __launch_bounds__(256) void bw_count_kernel(BwArgs a)
             else
                 hi = mid - 1;
         }
-        if (src >= 0) {
-            const __bf16 *dr = a.dense + (int64_t)src * a.F;
-            for (int c0 = 0; c0 < a.F; c0 += 64)
-                e += __popcll(__ballot(c0 + lane < a.F && (float)dr[c0 + lane] > 0.f));
+        if (src >= 0) {  // nonzeros of the dense row, 8 columns (16 bytes) per lane
+            const char *dr = reinterpret_cast<const char *>(a.dense + (int64_t)src * a.F);
+            const int nch = a.F / 8;
+            int mine = 0;
+            for (int c = lane; c < nch; c += 64) {
+                const u32x4 v = ldg16(dr + (int64_t)c * 16);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    mine += chunk_elem<__bf16>(v, q) > 0.f ? 1 : 0;
+            }
+            e = bw_wave_isum(mine);
         }
     }
     if (lane == 0) {
@@ -208,19 +215,30 @@ __global__ __launch_bounds__(256) void bw_entries_kernel(BwArgs a)
             a.ws.ent_h[p0 + k] = (float)a.val[slot];
         }
     } else if (src >= 0) {
-        const __bf16 *dr = a.dense + (int64_t)src * a.F;
+        // nonzeros of the dense row in ascending column: 8 columns per lane,
+        // a wave scan of the lanes' counts places them
+        const char *dr = reinterpret_cast<const char *>(a.dense + (int64_t)src * a.F);
+        const int nch = a.F / 8;
         int base = p0;
-        for (int c0 = 0; c0 < a.F; c0 += 64) {
+        for (int c0 = 0; c0 < nch; c0 += 64) {
             const int c = c0 + lane;
-            const float v = c < a.F ? (float)dr[c] : 0.f;
-            const uint64_t m = __ballot(v > 0.f);
-            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (v > 0.f) {
-                a.ws.ent_j[pos] = c;
-                a.ws.ent_h[pos] = v;
+            const u32x4 v = c < nch ? ldg16(dr + (int64_t)c * 16) : u32x4{0, 0, 0, 0};
+            int mine = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                mine += chunk_elem<__bf16>(v, q) > 0.f ? 1 : 0;
+            const int incl = bw_incl_scan(mine, lane);
+            int pos = base + incl - mine;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float h = chunk_elem<__bf16>(v, q);
+                if (h > 0.f) {
+                    a.ws.ent_j[pos] = c * 8 + q;
+                    a.ws.ent_h[pos] = h;
+                    ++pos;
+                }
             }
-            base += __popcll(m);
+            base += __shfl(incl, 63, 64);
         }
     }
 }
@@ -357,11 +375,18 @@ __global__ __launch_bounds__(256) void bw_colbase_kernel(BwArgs a)
     if (j >= a.F || a.ws.status[1])
         return;
     int run = 0;
-    for (int r = 0; r < a.n_rc; ++r) {
-        int32_t *p = a.ws.cnt_rc + (int64_t)r * a.F + j;
-        const int v = *p;
-        *p = run;
-        run += v;
+    int32_t *col = a.ws.cnt_rc + j;
+    for (int r0 = 0; r0 < a.n_rc; r0 += 16) {  // 16 loads in flight, then the stores
+        int v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            v[q] = r0 + q < a.n_rc ? col[(int64_t)(r0 + q) * a.F] : 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            if (r0 + q < a.n_rc)
+                col[(int64_t)(r0 + q) * a.F] = run;
+            run += v[q];
+        }
     }
     a.ws.col_ptr[j + 1] = run;
 }
