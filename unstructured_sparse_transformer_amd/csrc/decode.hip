@@ -256,13 +256,18 @@ __global__ __launch_bounds__(512) void pack_rows_kernel(PackArgs a)
         }
         a.row_e[t] = se;
         a.row_o[t] = so;
-        __threadfence();
-        s_last = atomicAdd(a.counter, 1) == (int)gridDim.x - 1;
+        if (gridDim.x == 1) {
+            s_last = 1;  // a single row: this workgroup is the last, no fences needed
+        } else {
+            __threadfence();
+            s_last = atomicAdd(a.counter, 1) == (int)gridDim.x - 1;
+        }
     }
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();
+    if (gridDim.x > 1)
+        __threadfence();
     if (wave != 0)
         return;
     // one lane per row (T <= 64)
