@@ -6,9 +6,20 @@ One step = the whole hot path over one batch, all on one HIP stream:
   twell_ffn_fused          fused up/down gather over the TwELL entries
   twell_ffn_overflow       dense FFN of the overflow rows (hybrid part)
 Inputs (seeded, synthetic, grid mode) are resident in HBM before timing.
+Untimed steps run for --settle-seconds (clocks out of idle), then --warmup
+steps, then the --steps timed ones back to back; timing events are HIP events
+with a device-scope release.
 
 Prints ONE JSON line (rank 0).  Default workload: the 2B-like layer
-(T=8192, d_model=2048, d_ff=8192, bf16, tile 256, capacity 16).
+(T=8192, d_model=2048, d_ff=8192, bf16, tile 256, capacity 16).  Besides the
+headline fields the line carries, each measured after the timed region:
+stages_ms (per-call breakdown), fused (gather bytes and rate), memory
+(TwELL / dense backup / compact / dense h bytes), gate_stats (the gate with
+activation statistics), conversions (hybrid <-> dense, compact storage),
+backward (twell_ffn_backward vs the dense bf16 backward), cold_cache_stages_ms,
+dense_bf16_ffn (torch on the same GPU), energy (board energy counter) and
+cpu_baseline (the oracle on the host cores).  --workload decode_<T> (T <= 64)
+times twell_ffn_decode instead; --workload stress_stack the 24-layer stack.
 """
 
 from __future__ import annotations

@@ -1,13 +1,20 @@
 /*
- * twell.h -- C ABI of libtwell: the ReLU-sparse gated FFN inference path on
- * MI355X (gfx950), with its activations held in TwELL (tile-wise ELLPACK).
+ * twell.h -- C ABI of libtwell: the ReLU-sparse gated FFN on MI355X
+ * (gfx950), with its activations held in TwELL (tile-wise ELLPACK).
  *
  * Source of the method: "Sparser, Faster, Lighter Transformer Language Models"
  * (gist.science summary page).  Section 2.1 defines TwELL and its production
  * in the gate matmul's epilogue; section 2.2 the fused up/down inference
  * kernel; section 2.3 the hybrid ELL + dense-backup format for rows whose
- * nonzeros do not fit.  The page gives no API; the calls below are this
- * library's own.
+ * nonzeros do not fit; section 2.4 the training side (conversions between the
+ * hybrid and dense activations, the L1 penalty on the activations).  The page
+ * gives no API; the calls below are this library's own:
+ *   inference   twell_pack_gate, twell_partition_overflow, twell_pack_gate_hybrid,
+ *               twell_ffn_fused, twell_ffn_overflow, twell_ffn_hybrid,
+ *               twell_ffn_decode (T <= 64)
+ *   statistics  twell_pack_gate_stats
+ *   training    twell_dense_to_hybrid, twell_hybrid_to_dense,
+ *               twell_compact_hybrid, twell_compact_to_dense, twell_ffn_backward
  *
  * Notation: T tokens (rows), d model width, F hidden width (d_ff), w tile
  * width, n_b = F / w tiles per row, cap = slots per (row, tile).
@@ -38,7 +45,7 @@
  *     returns TWELL_E_HIP.  Overflow is data, not an error.
  *   - No C++ exception crosses this interface; the library keeps no mutable
  *     global state.  Concurrent calls on different streams are safe when their
- *     output buffers do not overlap.
+ *     output and workspace buffers do not overlap.
  */
 #ifndef TWELL_H
 #define TWELL_H
