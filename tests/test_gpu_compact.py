@@ -118,3 +118,19 @@ def test_compact_layer_2b(gpu_lib):
     twell_bytes = wl.T * (wl.F // wl.tile_w) * (4 + wl.cap * 3)
     say(f"  compact {hdr['bytes']} B vs TwELL {twell_bytes} B + dense backup, dense h {wl.T * wl.F * 2} B")
     assert hdr["bytes"] < 0.05 * wl.T * wl.F * 2
+
+
+def test_compact_zero_rows(gpu_lib):
+    """T = 0: the buffer holds a header and row_ptr[0] = 0; expansion is a no-op."""
+    import torch
+    import unstructured_sparse_transformer_amd as tw
+    say("case compact T = 0")
+    hy = tw.Hybrid.empty(0, 512, 128, 8, torch.bfloat16, 0)
+    buf = torch.full((tw.twell_compact_min_bytes(0),), 0xEE, dtype=torch.uint8, device="cuda")
+    tw.twell_compact_hybrid(hy, buf)
+    hdr = tw.compact_header(buf)
+    assert hdr["T"] == 0 and hdr["n_entries"] == 0 and hdr["n_ovf"] == 0 and hdr["fits"] == 1
+    assert hdr["bytes"] == tw.twell_compact_min_bytes(0)
+    out = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    tw.twell_compact_to_dense(buf, 0, 512, torch.bfloat16, out)
+    torch.cuda.synchronize()

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(CP_SCAN_THREADS) void compact_scan_kernel(char *buf
     if (tid == 0) {
         const int esz = vdtype == 1 ? 2 : 4;
         const int n_entries = carry_s;
-        const int n = *n_ovf;
+        const int n = T > 0 ? *n_ovf : 0;  // with no rows the hybrid's pointers may be NULL
         const int nd = n < max_ovf ? n : max_ovf;
         CompactHdr h{};
         h.T = T;
@@ -246,11 +246,13 @@ static hipError_t compact_go(const int32_t *cnt, const void *val, const uint8_t 
 {
     const int n_b = F / tile_w;
     char *b = static_cast<char *>(buf);
-    compact_rows_count_kernel<<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, row_ovf, T, n_b,
-                                                                         reinterpret_cast<int32_t *>(b + 256));
+    if (T > 0)
+        compact_rows_count_kernel<<<dim3((T + 255) / 256), dim3(256), 0, s>>>(cnt, row_ovf, T, n_b,
+                                                                             reinterpret_cast<int32_t *>(b + 256));
     compact_scan_kernel<<<dim3(1), dim3(CP_SCAN_THREADS), 0, s>>>(b, buf_bytes, T, F, tile_w, vdtype, n_ovf, max_ovf);
-    compact_scatter_kernel<TI><<<dim3((T + 3) / 4), dim3(256), 0, s>>>(cnt, static_cast<const TI *>(val), idx,
-                                                                       row_ovf, T, n_b, tile_w, cap, b);
+    if (T > 0)
+        compact_scatter_kernel<TI><<<dim3((T + 3) / 4), dim3(256), 0, s>>>(cnt, static_cast<const TI *>(val), idx,
+                                                                           row_ovf, T, n_b, tile_w, cap, b);
     compact_dense_kernel<TI><<<dim3(max_ovf > 0 ? max_ovf : 1), dim3(256), 0, s>>>(static_cast<const TI *>(dense),
                                                                                   ovf_rows, max_ovf, F, b);
     return hipGetLastError();
