@@ -25,38 +25,9 @@
 #include "backward.h"
 #include "launch.h"
 #include "twell_device.h"
+#include "wave_ops.h"
 
 namespace twell {
-
-__device__ __forceinline__ float bw_wave_sum(float v)
-{
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));  // row_shr:1
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));  // row_shr:2
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));  // row_shr:4
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));  // row_shr:8
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));  // row_bcast:15
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));  // row_bcast:31
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-__device__ __forceinline__ int bw_wave_isum(int v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
-}
-
-__device__ __forceinline__ int bw_incl_scan(int v, int lane)
-{
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(v, o, 64);
-        if (lane >= o)
-            v += u;
-    }
-    return v;
-}
 
 // ------------------------------------------------------------------ counts
 // One wave per row: its entries and where they come from.  Also clears the
@@ -75,7 +46,7 @@ __global__ __launch_bounds__(256) void bw_count_kernel(BwArgs a)
     if (!a.row_ovf[t]) {
         const int32_t *crow = a.cnt + (int64_t)t * a.n_b;
         for (int b0 = 0; b0 < a.n_b; b0 += 64)
-            e += bw_wave_isum(b0 + lane < a.n_b ? crow[b0 + lane] : 0);
+            e += wave_isum(b0 + lane < a.n_b ? crow[b0 + lane] : 0);
     } else {
         const int nd = *a.n_ovf < a.max_ovf ? *a.n_ovf : a.max_ovf;
         int lo = 0, hi = nd - 1;
@@ -102,7 +73,7 @@ __global__ __launch_bounds__(256) void bw_count_kernel(BwArgs a)
                 for (int q = 0; q < 8; ++q)
                     mine += chunk_elem<__bf16>(v, q) > 0.f ? 1 : 0;
             }
-            e = bw_wave_isum(mine);
+            e = wave_isum(mine);
         }
     }
     if (lane == 0) {
@@ -127,7 +98,7 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a)
         const int t = base + tid;
         const int e = t < a.T ? a.ws.row_e[t] : 0;
         const int c = (e + BW_CE - 1) / BW_CE;
-        const int ie = bw_incl_scan(e, lane), ic = bw_incl_scan(c, lane);
+        const int ie = wave_incl_scan(e, lane), ic = wave_incl_scan(c, lane);
         if (lane == 63) {
             wt[0][wave] = ie;
             wt[1][wave] = ic;
@@ -192,7 +163,7 @@ __global__ __launch_bounds__(256) void bw_entries_kernel(BwArgs a)
         for (int b0 = 0; b0 < a.n_b; b0 += 64) {
             const int b = b0 + lane;
             const int c = b < a.n_b ? crow[b] : 0;
-            const int incl = bw_incl_scan(c, lane);
+            const int incl = wave_incl_scan(c, lane);
             if (b < a.n_b)
                 sp[b] = run + incl - c;
             run += __shfl(incl, 63, 64);
@@ -227,7 +198,7 @@ __global__ __launch_bounds__(256) void bw_entries_kernel(BwArgs a)
 #pragma unroll
             for (int q = 0; q < 8; ++q)
                 mine += chunk_elem<__bf16>(v, q) > 0.f ? 1 : 0;
-            const int incl = bw_incl_scan(mine, lane);
+            const int incl = wave_incl_scan(mine, lane);
             int pos = base + incl - mine;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -280,7 +251,7 @@ __device__ __forceinline__ void bw_apply(const BwArgs &a, const BwRows<NC> &r, i
             su = fmaf(xf[c][e], chunk_elem<__bf16>(r.wu[c], e), su);
             sg = fmaf(gf[c][e], chunk_elem<__bf16>(r.wd[c], e), sg);
         }
-    const float u = bw_wave_sum(su), g = bw_wave_sum(sg);
+    const float u = wave_sum(su), g = wave_sum(sg);
     const float du = g * h, dz = g * u;
     if (lane == 0) {
         a.ws.ent_du[k] = du;
@@ -408,7 +379,7 @@ __global__ __launch_bounds__(1024) void bw_colscan_kernel(BwArgs a)
     for (int base = 0; base < a.F; base += 1024) {
         const int j = base + tid;
         const int v = j < a.F ? a.ws.col_ptr[j + 1] : 0;
-        const int incl = bw_incl_scan(v, lane);
+        const int incl = wave_incl_scan(v, lane);
         if (lane == 63)
             wt[wave] = incl;
         __syncthreads();

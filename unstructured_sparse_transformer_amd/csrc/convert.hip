@@ -20,6 +20,7 @@
 //     rows.
 #include "launch.h"
 #include "twell_device.h"
+#include "wave_ops.h"
 
 namespace twell {
 
@@ -31,32 +32,6 @@ template <typename TI> struct ConvArgs {
     int32_t *cnt;
     int32_t *row_ovf, *work;  // dense -> hybrid: per-row flag and stored entries (0 if flagged)
 };
-
-// Inclusive scan of v over segments of L lanes (L a power of two, <= 64; gl =
-// lane within its segment): DPP row shifts inside 16-lane rows (masked at
-// segment starts when L < 16), then row broadcasts across rows.
-__device__ __forceinline__ int seg_incl_scan(int v, int gl, int L)
-{
-    int y = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-    v += gl >= 1 ? y : 0;
-    if (L > 2) {
-        y = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-        v += gl >= 2 ? y : 0;
-    }
-    if (L > 4) {
-        y = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-        v += gl >= 4 ? y : 0;
-    }
-    if (L > 8) {
-        y = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-        v += gl >= 8 ? y : 0;
-    }
-    if (L > 16)
-        v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-    if (L > 32)
-        v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
-    return v;
-}
 
 // Row t; lane l of a wave pass owns CPL = 16 / sizeof(TI) consecutive columns
 // (one 16-byte load), so a pass covers 64 * CPL columns = 64 * CPL / w whole

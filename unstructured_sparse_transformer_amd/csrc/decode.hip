@@ -13,6 +13,7 @@
 #include "decode.h"
 #include "launch.h"
 #include "twell_device.h"
+#include "wave_ops.h"
 
 namespace twell {
 
@@ -164,19 +165,6 @@ __device__ __forceinline__ int chunk_entries(int total)
 __device__ __forceinline__ int work_class_of(int e)
 {
     return e >= 256 ? 0 : e >= 192 ? 1 : e >= 128 ? 2 : e >= 64 ? 3 : e >= 32 ? 4 : e >= 16 ? 5 : e >= 1 ? 6 : 7;
-}
-
-__device__ __forceinline__ int wave_excl_scan(int v, int lane, int &total)
-{
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, 64);
-        if (lane >= o)
-            incl += u;
-    }
-    total = __shfl(incl, 63, 64);
-    return incl - v;
 }
 
 // Pack tile b of row t (all lanes of the wave); returns its true count.

@@ -21,6 +21,7 @@
 #include "decode.h"
 #include "launch.h"
 #include "twell_device.h"
+#include "wave_ops.h"
 
 #ifndef FUSED_G
 #define FUSED_G 2
@@ -43,39 +44,6 @@ template <typename TI> struct FusedArgs {
     int d, nchunks;  // nchunks = 16-byte chunks per row
     float *y;
 };
-
-// Sum over the 64 lanes with DPP row shifts and row broadcasts (an inclusive
-// scan whose last lane holds the total), returned as a wave-uniform value.
-// The order of the additions is fixed, so the result is deterministic.
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));  // row_shr:1
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));  // row_shr:2
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));  // row_shr:4
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));  // row_shr:8
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));  // row_bcast:15
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));  // row_bcast:31
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-__device__ __forceinline__ int wave_isum(int v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane)
-{
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(v, o, 64);
-        if (lane >= o)
-            v += u;
-    }
-    return v;
-}
 
 // Weight rows of G list entries in registers.
 template <typename TI, int NC, int G> struct Group {

@@ -15,6 +15,7 @@
 // workgroups past it return at once.
 #include "launch.h"
 #include "twell_device.h"
+#include "wave_ops.h"
 
 namespace twell {
 
@@ -45,19 +46,6 @@ __global__ __launch_bounds__(256) void row_flags_kernel(const int32_t *__restric
     }
     row_ovf[t] = f;
     work[t] = f ? 0 : e;
-}
-
-// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
-// broadcasts (lanes shifted in from outside a row contribute 0).
-__device__ __forceinline__ int wave_incl_scan_dpp(int v)
-{
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
-    return v;
 }
 
 // Work classes of the fused step's schedule, heaviest = 7.
