@@ -1,10 +1,12 @@
 """Benchmark: sparse-FFN tokens/s of the TwELL path on one MI355X.
 
-One step = the whole hot path over one batch, all on one HIP stream:
+One step = the whole hot path over one batch, all on one HIP stream, in two
+calls (together the same as one twell_ffn_forward):
   twell_pack_gate          gate GEMM (bf16 MFMA) + ReLU + TwELL epilogue
-  twell_partition_overflow overflow flags, ascending overflow list, dense backup
-  twell_ffn_fused          fused up/down gather over the TwELL entries
-  twell_ffn_overflow       dense FFN of the overflow rows (hybrid part)
+  twell_ffn_from_gate      overflow flags, ascending overflow list and work
+                           order; the fused up/down gather over the TwELL
+                           entries; one GEMM for the dense backup and the
+                           overflow rows' up projection; their down projection
 Inputs (seeded, synthetic, grid mode) are resident in HBM before timing.
 Untimed steps run for --settle-seconds (clocks out of idle), then --warmup
 steps, then the --steps timed ones back to back; timing events are HIP events
@@ -13,7 +15,8 @@ with a device-scope release.
 Prints ONE JSON line (rank 0).  Default workload: the 2B-like layer
 (T=8192, d_model=2048, d_ff=8192, bf16, tile 256, capacity 16).  Besides the
 headline fields the line carries, each measured after the timed region:
-stages_ms (per-call breakdown), fused (gather bytes and rate), memory
+stages_ms (the two calls, and the layer through the separate calls
+twell_partition_overflow / twell_ffn_fused / twell_ffn_overflow), fused (gather bytes and rate), memory
 (TwELL / dense backup / compact / dense h bytes), gate_stats (the gate with
 activation statistics), conversions (hybrid <-> dense, compact storage),
 backward (twell_ffn_backward vs the dense bf16 backward), cold_cache_stages_ms,
@@ -157,7 +160,7 @@ def measured_traffic(kernel, workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not implemented", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
@@ -203,29 +206,32 @@ def main():
         log("calibration: 3 x fp32 multiply, 268435456 B read + 268435456 B written each")
         del src, dst
 
-    def step(ev=None):
-        if ev:
-            ev[0].record()
+    # One step = the layer: the gate (TwELL packing) and the rest of the layer
+    # in a second call (twell_ffn_forward in two parts, so that the gate kernel
+    # can be bracketed by events)
+    def step():
         tw.twell_pack_gate(x, wg, hy.ell)
-        if ev:
-            ev[1].record()
-        tw.twell_partition_overflow(x, wg, hy)
-        if ev:
-            ev[2].record()
-        tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=hy.order)
-        if ev:
-            ev[3].record()
-        tw.twell_ffn_overflow(hy, x, wu, wd, y, ws)
-        if ev:
-            ev[4].record()
+        tw.twell_ffn_from_gate(x, wg, wu, wd, hy, y, ws)
 
     def step_gate_events(ev):
         ev[0].record()
         tw.twell_pack_gate(x, wg, hy.ell)
         ev[1].record()
+        tw.twell_ffn_from_gate(x, wg, wu, wd, hy, y, ws)
+
+    # The same layer through the separate calls, events between them (the
+    # per-call breakdown; there the dense backup and the overflow rows' up
+    # projection are two GEMMs, one in each of the last two calls)
+    def split_step(ev):
+        ev[0].record()
+        tw.twell_pack_gate(x, wg, hy.ell)
+        ev[1].record()
         tw.twell_partition_overflow(x, wg, hy)
+        ev[2].record()
         tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=hy.order)
+        ev[3].record()
         tw.twell_ffn_overflow(hy, x, wu, wd, y, ws)
+        ev[4].record()
 
     # one step for the workload's statistics (host reads), then the settle and
     # warmup steps right before the timed region, with no idle gap between
@@ -258,9 +264,18 @@ def main():
     value = wl.T * args.steps / wall
 
     # ---- per-stage breakdown (after the timed region; events between all stages)
+    sev = [[DevEvent() for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        sev[k][0].record()
+        tw.twell_pack_gate(x, wg, hy.ell)
+        sev[k][1].record()
+        tw.twell_ffn_from_gate(x, wg, wu, wd, hy, y, ws)
+        sev[k][2].record()
+    torch.cuda.synchronize()
+    main_ms = np.array([[sev[k][i].elapsed_time(sev[k][i + 1]) for i in range(2)] for k in range(args.steps)]).mean(0)
     sev = [[DevEvent() for _ in range(5)] for _ in range(args.steps)]
     for k in range(args.steps):
-        step(sev[k])
+        split_step(sev[k])
     torch.cuda.synchronize()
     stage = np.array([[sev[k][i].elapsed_time(sev[k][i + 1]) for i in range(4)] for k in range(args.steps)])
     stage_ms = stage.mean(0)
@@ -304,9 +319,12 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
                    "cap": wl.cap, "max_ovf": max_ovf, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
-        "stages_ms": {"pack_gate": round(float(stage_ms[0]), 4), "partition_overflow": round(float(stage_ms[1]), 4),
-                      "ffn_fused": round(float(stage_ms[2]), 4), "ffn_overflow": round(float(stage_ms[3]), 4),
-                      "note": "separate pass after the timed region, events between all stages"},
+        "stages_ms": {"pack_gate": round(float(main_ms[0]), 4), "ffn_from_gate": round(float(main_ms[1]), 4),
+                      "split_calls": {"pack_gate": round(float(stage_ms[0]), 4),
+                                      "partition_overflow": round(float(stage_ms[1]), 4),
+                                      "ffn_fused": round(float(stage_ms[2]), 4),
+                                      "ffn_overflow": round(float(stage_ms[3]), 4)},
+                      "note": "separate passes after the timed region, events between the calls"},
         "fused": fused,
         "workload_stats": {"nnz": nnz, "n_ovf": n_ovf, "twell_entries": entries, "union_active_twell": union,
                            "mean_active_per_token": round(nnz / wl.T, 2)},
@@ -434,15 +452,14 @@ def main():
         cold = []
         for k in range(min(args.steps, 10)):
             flush.fill_(float(k))
-            ev = [DevEvent() for _ in range(5)]
-            step(ev)
+            ev = [DevEvent() for _ in range(3)]
+            step_gate_events(ev)
+            ev[2].record()
             torch.cuda.synchronize()
-            cold.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
+            cold.append([ev[i].elapsed_time(ev[i + 1]) for i in range(2)])
         cold = np.array(cold).mean(0)
         out["cold_cache_stages_ms"] = {"pack_gate": round(float(cold[0]), 4),
-                                       "partition_overflow": round(float(cold[1]), 4),
-                                       "ffn_fused": round(float(cold[2]), 4),
-                                       "ffn_overflow": round(float(cold[3]), 4),
+                                       "ffn_from_gate": round(float(cold[1]), 4),
                                        "tokens_per_s": round(wl.T / (cold.sum() * 1e-3), 1)}
         del flush
 
@@ -550,7 +567,7 @@ def energy_per_token(fns, tokens_per_call, seconds, torch):
 def run_decode(args, wl, tw, torch, np):
     """Decode-shaped calls (T <= 64, bf16): one twell_ffn_decode call per step
     (gate, packing and partition, chunked gather, reduction: 4 kernels), next
-    to the batch path's four calls and the dense bf16 FFN on the same rows.
+    to the batch path (twell_ffn_forward) and the dense bf16 FFN on the same rows.
     Roofline: the step is bound by HBM; its algorithmic bytes are W_g read
     once, the W_u / W_d rows of every active (row, neuron), x, y and the TwELL
     written."""
@@ -591,8 +608,7 @@ def run_decode(args, wl, tw, torch, np):
     wsb = tw.hybrid_workspace(wl.T, wl.F, wl.d, torch.bfloat16)
 
     def batch():
-        tw.twell_pack_gate_hybrid(x, wg, hb)
-        tw.twell_ffn_hybrid(hb, x, wu, wd, y, wsb)
+        tw.twell_ffn_forward(x, wg, wu, wd, hb, y, wsb)
 
     _, ms_batch = timed(batch, args.steps)
     out = {
@@ -643,9 +659,7 @@ def run_stack(args, tw, torch, np):
             tw.twell_pack_gate(x, wg, hy.ell)
             if ev:
                 ev[1].record()
-            tw.twell_partition_overflow(x, wg, hy)
-            tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=hy.order)
-            tw.twell_ffn_overflow(hy, x, wu, wd, y, ws)
+            tw.twell_ffn_from_gate(x, wg, wu, wd, hy, y, ws)
 
         if layer == 0:  # later layers follow without idle gaps
             settle(step, args.settle_seconds, torch)

@@ -9,7 +9,9 @@
  * nonzeros do not fit; section 2.4 the training side (conversions between the
  * hybrid and dense activations, the L1 penalty on the activations).  The page
  * gives no API; the calls below are this library's own:
- *   inference   twell_pack_gate, twell_partition_overflow, twell_pack_gate_hybrid,
+ *   inference   twell_ffn_forward (the whole layer in one call),
+ *               twell_ffn_from_gate (the layer after twell_pack_gate[_stats]),
+ *               twell_pack_gate, twell_partition_overflow, twell_pack_gate_hybrid,
  *               twell_ffn_fused, twell_ffn_overflow, twell_ffn_hybrid,
  *               twell_ffn_decode (T <= 64)
  *   statistics  twell_pack_gate_stats
@@ -181,6 +183,29 @@ TWELL_API int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const 
  * full FFN output when n_ovf <= max_ovf. */
 TWELL_API int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
                      int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The whole layer in one call (sections 2.1-2.3 of the page): the hybrid of
+ * the gate activation (as twell_pack_gate_hybrid writes it: TwELL, row_ovf,
+ * ovf_rows, n_ovf, order, dense backup) and y (as twell_ffn_hybrid writes it),
+ * bit for bit the same as those two calls.  The dense backup and the
+ * overflow rows' up projection come from one GEMM over the gathered x rows
+ * (W_g^T and W_u^T tiles side by side) instead of two.
+ *   x, wg_t, wu_t, wd : device, vdtype hy->ell.vdtype, 16-byte aligned;
+ *   y : device [T][d] float; workspace: device, >=
+ *   twell_ffn_hybrid_workspace_bytes(hy->max_ovf, F, d, vdtype), 256-byte
+ *   aligned (may be NULL when that is 0), content ignored on entry.
+ *   Every check is made before the first launch. */
+TWELL_API int twell_ffn_forward(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                      const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* twell_ffn_forward without its first step: hy->ell holds the TwELL of
+ * x . W_g already (twell_pack_gate or twell_pack_gate_stats on the same
+ * stream); writes the rest of the hybrid and y.  Same arguments and checks;
+ * twell_ffn_forward = twell_pack_gate + twell_ffn_from_gate. */
+TWELL_API int twell_ffn_from_gate(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                        const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes,
+                        void *stream);
 
 /* Dense activations to the hybrid (section 2.4 of the page: the conversion
  * kernels training uses in the forward and backward passes).  h : device

@@ -43,8 +43,35 @@ def _offset_views(hy, dt):
     ell.cnt = torch.empty(nc + 4, dtype=torch.int32, device="cuda")[1:1 + nc].view(ell.cnt.shape)
 
 
+def _poison(hy, T, d):
+    import torch
+    hy.ell.cnt.fill_(-7)
+    hy.ell.idx.fill_(0xAB)
+    hy.ell.val.fill_(-3.0)
+    hy.row_ovf.fill_(-7)
+    hy.n_ovf.fill_(-7)
+    hy.order.fill_(-7)
+    return torch.full((T, d), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def _check_forward(hy, y, hy1, y1, m):
+    """twell_ffn_forward's (or pack_gate + twell_ffn_from_gate's) outputs equal
+    the separate calls' bit for bit."""
+    import torch
+    for name, a, b in (("cnt", hy.ell.cnt, hy1.ell.cnt), ("idx", hy.ell.idx, hy1.ell.idx),
+                       ("val", hy.ell.val, hy1.ell.val), ("row_ovf", hy.row_ovf, hy1.row_ovf),
+                       ("n_ovf", hy.n_ovf, hy1.n_ovf), ("order", hy.order, hy1.order),
+                       ("ovf_rows", hy.ovf_rows[:m], hy1.ovf_rows[:m]), ("dense", hy.dense[:m], hy1.dense[:m])):
+        assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), \
+            f"twell_ffn_forward differs from the separate calls in {name}"
+    assert torch.equal(y.view(torch.int32), y1.view(torch.int32)), \
+        "twell_ffn_forward differs from the separate calls in y"
+
+
 def run_hip(wl, max_ovf=None, stream=None, unaligned=False):
-    """Run pack_gate_hybrid + ffn_hybrid and (separately) ffn_fused; return host arrays."""
+    """Run pack_gate_hybrid + ffn_hybrid and (separately) ffn_fused; return host arrays.
+    Also runs twell_ffn_forward into fresh buffers and checks that it writes the
+    same bits as pack_gate_hybrid + ffn_hybrid."""
     import torch
     import unstructured_sparse_transformer_amd as tw
     dt, x, wg, wu, wd = to_device(wl)
@@ -68,9 +95,20 @@ def run_hip(wl, max_ovf=None, stream=None, unaligned=False):
     tw.twell_ffn_hybrid(hy, x, wu, wd, y, ws, stream)
     tw.twell_ffn_fused(hy.ell, x, wu, wd, yf, stream)                 # ascending rows
     tw.twell_ffn_fused(hy.ell, x, wu, wd, yo, stream, order=hy.order)  # work order
+    hy2 = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
+    if unaligned:
+        _offset_views(hy2, dt)
+    y2 = _poison(hy2, wl.T, wl.d)
+    tw.twell_ffn_forward(x, wg, wu, wd, hy2, y2, tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt), stream)
+    hy3 = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
+    y3 = _poison(hy3, wl.T, wl.d)
+    tw.twell_pack_gate(x, wg, hy3.ell, stream)
+    tw.twell_ffn_from_gate(x, wg, wu, wd, hy3, y3, tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt), stream)
     torch.cuda.synchronize()
     n_ovf = int(hy.n_ovf.item())
     m = min(n_ovf, max_ovf)
+    _check_forward(hy2, y2, hy, y, m)
+    _check_forward(hy3, y3, hy, y, m)
     return {
         "cnt": hy.ell.cnt.cpu().numpy(),
         "val": hy.ell.val.float().cpu().numpy(),

@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 105
+    assert lib.twell_version() == 106
 
 
 def test_status_strings():
@@ -101,6 +101,39 @@ def test_fused_and_hybrid_validation():
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, ctypes.byref(odd), None) == -2
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, None, None) == -1
     assert lib.twell_ffn_hybrid_workspace_bytes(0, 512, 64, 1) == 0
+
+
+def test_ffn_forward_validation():
+    """Every argument of the one-call layer is checked before its first launch."""
+    lib = tw.load()
+    f = lib.twell_ffn_forward
+    d = _desc()
+    hy = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
+    r = ctypes.byref(hy)
+    need = lib.twell_ffn_hybrid_workspace_bytes(8, 512, 64, 1)
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, None, GOOD, GOOD, need, None) == -1          # hybrid NULL
+    assert f(None, GOOD, GOOD, GOOD, 64, r, GOOD, GOOD, need, None) == -1             # x NULL
+    assert f(GOOD, None, GOOD, GOOD, 64, r, GOOD, GOOD, need, None) == -1             # W_g NULL
+    assert f(GOOD, GOOD, None, GOOD, 64, r, GOOD, GOOD, need, None) == -1             # W_u NULL
+    assert f(GOOD, GOOD, GOOD, None, 64, r, GOOD, GOOD, need, None) == -1             # W_d NULL
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, r, None, GOOD, need, None) == -1             # y NULL
+    assert f(GOOD, GOOD, GOOD + 2, GOOD, 64, r, GOOD, GOOD, need, None) == -2         # W_u misaligned
+    assert f(GOOD, GOOD, GOOD, GOOD, 60, r, GOOD, GOOD, need, None) == -3             # d % 64
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, r, GOOD, None, 0, None) == -6                # no workspace
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, r, GOOD, GOOD, need - 1, None) == -6         # too small
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, r, GOOD, GOOD + 16, need, None) == -2        # not 256-aligned
+    nod = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, None, GOOD)                     # dense NULL
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(nod), GOOD, GOOD, need, None) == -1
+    noval = tw.TwellHybridT(_desc(val=0), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)         # TwELL val NULL
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(noval), GOOD, GOOD, need, None) == -1
+    empty = tw.TwellHybridT(_desc(T=0), 8, 0, None, None, None, None, None)
+    assert f(None, None, None, None, 64, ctypes.byref(empty), None, None, 0, None) == 0  # T = 0
+    g = lib.twell_ffn_from_gate  # same checks
+    assert g(GOOD, GOOD, GOOD, GOOD, 64, None, GOOD, GOOD, need, None) == -1
+    assert g(GOOD, None, GOOD, GOOD, 64, r, GOOD, GOOD, need, None) == -1
+    assert g(GOOD, GOOD, GOOD, GOOD, 64, r, GOOD, GOOD, need - 1, None) == -6
+    assert g(GOOD, GOOD, GOOD, GOOD, 64, r, GOOD + 4, GOOD, need, None) == -2
+    assert g(None, None, None, None, 64, ctypes.byref(empty), None, None, 0, None) == 0
 
 
 def test_ffn_decode_validation():

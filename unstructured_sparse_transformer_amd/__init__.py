@@ -6,7 +6,8 @@ memory and the current HIP stream.  There is no CPU fallback: ``load()``
 raises when the library is missing, and every call raises on a non-OK status.
 
 The functions carry the C names (``include/twell.h``):
-``twell_pack_gate``, ``twell_pack_gate_stats``, ``twell_partition_overflow``, ``twell_pack_gate_hybrid``,
+``twell_ffn_forward``, ``twell_ffn_from_gate``, ``twell_pack_gate``, ``twell_pack_gate_stats``, ``twell_partition_overflow``,
+``twell_pack_gate_hybrid``,
 ``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
 ``twell_ffn_hybrid_workspace_bytes``, ``twell_ffn_decode``,
 ``twell_ffn_decode_workspace_bytes``, ``twell_dense_to_hybrid``,
@@ -27,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libtwell.so")
 TWELL_F32, TWELL_BF16 = 0, 1
 STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_SHAPE",
           -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE"}
-EXPORTS = ("twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
+EXPORTS = ("twell_ffn_forward", "twell_ffn_from_gate", "twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
            "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
            "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_dense_to_hybrid", "twell_hybrid_to_dense",
            "twell_compact_min_bytes", "twell_compact_hybrid", "twell_compact_to_dense",
@@ -75,6 +76,8 @@ def load(path: str = LIB_PATH):
     lib.twell_ffn_hybrid_workspace_bytes.restype = ctypes.c_size_t
     lib.twell_ffn_hybrid.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
     lib.twell_ffn_overflow.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
+    lib.twell_ffn_forward.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P, ctypes.c_size_t, P]
+    lib.twell_ffn_from_gate.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P, ctypes.c_size_t, P]
     lib.twell_ffn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.twell_ffn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.twell_ffn_decode.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P, ctypes.c_size_t, P]
@@ -92,7 +95,8 @@ def load(path: str = LIB_PATH):
     lib.twell_status_str.restype = ctypes.c_char_p
     lib.twell_version.restype = ctypes.c_int
     for fn in (lib.twell_pack_gate, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
-               lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_decode,
+               lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_forward,
+               lib.twell_ffn_from_gate, lib.twell_ffn_decode,
                lib.twell_dense_to_hybrid, lib.twell_hybrid_to_dense, lib.twell_compact_hybrid,
                lib.twell_compact_to_dense, lib.twell_ffn_backward):
         fn.restype = ctypes.c_int
@@ -227,6 +231,24 @@ def twell_ffn_hybrid(hy: Hybrid, x, wu_t, wd, y, workspace, stream=None):
     _check("twell_ffn_hybrid",
            lib.twell_ffn_hybrid(ctypes.byref(hy.desc()), _ptr(x), _ptr(wu_t), _ptr(wd), int(x.shape[1]),
                                 _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def twell_ffn_forward(x, wg_t, wu_t, wd, hy: Hybrid, y, workspace, stream=None):
+    """The whole layer: fills the hybrid `hy` and y [T][d] float in one call."""
+    lib = load()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("twell_ffn_forward",
+           lib.twell_ffn_forward(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), int(x.shape[1]), ctypes.byref(hy.desc()),
+                                 _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def twell_ffn_from_gate(x, wg_t, wu_t, wd, hy: Hybrid, y, workspace, stream=None):
+    """The layer after twell_pack_gate on hy.ell: the rest of the hybrid and y."""
+    lib = load()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("twell_ffn_from_gate",
+           lib.twell_ffn_from_gate(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), int(x.shape[1]),
+                                   ctypes.byref(hy.desc()), _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def twell_ffn_overflow(hy: Hybrid, x, wu_t, wd, y, workspace, stream=None):

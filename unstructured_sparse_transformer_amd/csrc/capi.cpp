@@ -95,9 +95,58 @@ size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
 
 }  // namespace
 
+namespace {
+
+// Checks shared by twell_ffn_from_gate and twell_ffn_forward (T > 0).
+int check_layer(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                const twell_hybrid_t *hy, const float *y, const void *workspace, size_t workspace_bytes)
+{
+    const twell_t *h = &hy->ell;
+    TWELL_TRY(check_ptrs(h));
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wg_t));
+    TWELL_TRY(check_mat(wu_t));
+    TWELL_TRY(check_mat(wd));
+    TWELL_TRY(check_mat(y));
+    const size_t need = twell_ffn_hybrid_workspace_bytes(hy->max_ovf, h->F, d, h->vdtype);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return TWELL_E_WORKSPACE;
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return TWELL_E_ALIGN;
+    return TWELL_OK;
+}
+
+// The layer after the gate, arguments already checked: overflow flags,
+// overflow list and work order, the fused step, then the dense backup and
+// gated up product of the overflow rows in one GEMM, and their down projection.
+int launch_from_gate(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                     const twell_hybrid_t *hy, float *y, void *workspace, hipStream_t s)
+{
+    const twell_t *h = &hy->ell;
+    const int n_b = h->F / h->tile_w;
+    TWELL_TRY(hip_status(twell::launch_row_flags(h->cnt, h->T, n_b, h->cap, hy->row_ovf, hy->order, s)));
+    TWELL_TRY(hip_status(
+        twell::launch_compact_rows(hy->row_ovf, h->T, hy->max_ovf, hy->ovf_rows, hy->n_ovf, hy->order, s)));
+    TWELL_TRY(hip_status(twell::launch_ffn_fused(h->vdtype, h->cnt, h->val, h->idx, hy->order, h->T, h->F,
+                                                 h->tile_w, h->cap, x, wu_t, wd, d, y, s)));
+    if (hy->max_ovf == 0)
+        return TWELL_OK;
+    char *ws = static_cast<char *>(workspace);
+    void *pbuf = ws;
+    const int splits = twell::down_splits(hy->max_ovf, h->F, d);
+    float *part = splits > 1 ? reinterpret_cast<float *>(ws + hybrid_ws_p_bytes(hy->max_ovf, h->F, h->vdtype))
+                             : nullptr;
+    TWELL_TRY(hip_status(twell::launch_dense_gate_up(h->vdtype, x, h->T, wg_t, wu_t, hy->ovf_rows, hy->n_ovf,
+                                                     hy->max_ovf, d, h->F, hy->dense, pbuf, s)));
+    return hip_status(twell::launch_down(h->vdtype, pbuf, wd, hy->ovf_rows, hy->n_ovf, hy->max_ovf, h->F, d, y, part,
+                                         splits, s));
+}
+
+}  // namespace
+
 extern "C" {
 
-int twell_version(void) { return 105; }
+int twell_version(void) { return 106; }
 
 const char *twell_status_str(int status)
 {
@@ -449,6 +498,37 @@ int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, 
         return TWELL_E_ALIGN;
     TWELL_TRY(twell_ffn_fused(h, hy->order, x, wu_t, wd, d, y, stream));
     return twell_ffn_overflow(hy, x, wu_t, wd, d, y, workspace, workspace_bytes, stream);
+}
+
+int twell_ffn_from_gate(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                        const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    TWELL_TRY(check_layout(&hy->ell, d));
+    TWELL_TRY(check_hybrid(hy));
+    if (hy->ell.T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_layer(x, wg_t, wu_t, wd, d, hy, y, workspace, workspace_bytes));
+    return launch_from_gate(x, wg_t, wu_t, wd, d, hy, y, workspace, static_cast<hipStream_t>(stream));
+}
+
+int twell_ffn_forward(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                      const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *h = &hy->ell;
+    TWELL_TRY(check_layout(h, d));
+    TWELL_TRY(check_hybrid(hy));
+    if (h->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_layer(x, wg_t, wu_t, wd, d, hy, y, workspace, workspace_bytes));
+    // every argument is checked: from here on only launches
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TWELL_TRY(hip_status(twell::launch_gate_twell(h->vdtype, x, wg_t, h->T, d, h->F, h->tile_w, h->cap, h->val,
+                                                  h->idx, h->cnt, s)));
+    return launch_from_gate(x, wg_t, wu_t, wd, d, hy, y, workspace, s);
 }
 
 }  // extern "C"

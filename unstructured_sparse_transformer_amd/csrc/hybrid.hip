@@ -54,10 +54,10 @@ __device__ __forceinline__ int work_class(int e)
     return e == 0 ? 0 : e < 16 ? 1 : e < 32 ? 2 : e < 64 ? 3 : e < 128 ? 4 : e < 192 ? 5 : e < 256 ? 6 : 7;
 }
 
-// One workgroup, per chunk of 16384 rows: the rows' flags and work classes
-// are read with coalesced loads into a byte per row in LDS; thread i then
-// owns rows [16 i, 16 i + 16) of the chunk.  Nine per-thread counts (flagged
-// rows; rows of each work class) go through one workgroup exclusive scan (DPP
+// One workgroup, per chunk of 16384 rows: thread i owns rows [16 i, 16 i + 16)
+// of the chunk and reads their flags and work values with one batch of
+// loads (16-byte vectors when VEC).  Nine per-thread counts (flagged rows;
+// rows of each work class) go through one workgroup exclusive scan (DPP
 // wave scans + 16 wave totals in LDS); each thread writes its flagged rows to
 // the ascending overflow list and its rows to their places in the chunk's
 // work order (classes from the heaviest, ascending rows inside a class),
@@ -67,6 +67,7 @@ __device__ __forceinline__ int work_class(int e)
 // number of flagged rows.
 constexpr int CR_THREADS = 1024, CR_ROWS = 16, CR_NC = 8, CR_CHUNK = CR_THREADS * CR_ROWS;
 
+template <bool VEC>
 __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t *__restrict__ row_ovf, int T,
                                                                   int max_ovf, int32_t *__restrict__ ovf_rows,
                                                                   int32_t *__restrict__ n_ovf, int32_t *order)
@@ -75,30 +76,37 @@ __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t 
     constexpr int NW = CR_THREADS / 64;
     __shared__ int wave_tot[NW][NV];
     __shared__ int wave_off[NW + 1][NV];  // exclusive prefix over waves; row NW = totals
-    __shared__ __attribute__((aligned(16))) uint8_t srow[CR_CHUNK];  // bit 7: flagged; bits 0-2: class
-    __shared__ int sord[CR_CHUNK];                                   // the chunk's work order
+    __shared__ int sord[CR_CHUNK];        // the chunk's work order
     const int tid = threadIdx.x, wave = tid >> 6;
     int base = 0;
     for (int t0 = 0; t0 < T; t0 += CR_CHUNK) {
         const int nrows = T - t0 < CR_CHUNK ? T - t0 : CR_CHUNK;
-#pragma unroll 4
-        for (int k = 0; k < CR_ROWS; ++k) {
-            const int i = k * CR_THREADS + tid;
-            if (i < nrows)
-                srow[i] = (uint8_t)((row_ovf[t0 + i] != 0 ? 0x80 : 0) | work_class(order[t0 + i]));
-        }
-        __syncthreads();
         const int i0 = tid * CR_ROWS;
-        const u32x4 rb = *reinterpret_cast<const u32x4 *>(srow + i0);
+        int fl[CR_ROWS], wk[CR_ROWS];
+        if (VEC && i0 + CR_ROWS <= nrows) {
+#pragma unroll
+            for (int q = 0; q < CR_ROWS / 4; ++q) {
+                const int4 f4 = *reinterpret_cast<const int4 *>(row_ovf + t0 + i0 + 4 * q);
+                const int4 w4 = *reinterpret_cast<const int4 *>(order + t0 + i0 + 4 * q);
+                fl[4 * q] = f4.x, fl[4 * q + 1] = f4.y, fl[4 * q + 2] = f4.z, fl[4 * q + 3] = f4.w;
+                wk[4 * q] = w4.x, wk[4 * q + 1] = w4.y, wk[4 * q + 2] = w4.z, wk[4 * q + 3] = w4.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < CR_ROWS; ++k) {
+                const bool in = i0 + k < nrows;
+                fl[k] = in ? row_ovf[t0 + i0 + k] : 0;
+                wk[k] = in ? order[t0 + i0 + k] : 0;
+            }
+        }
         uint32_t bits = 0;
         uint64_t cls = 0;   // 4 bits per row: its work class
         uint64_t ccnt = 0;  // 8 bits per class: rows of this thread in it
 #pragma unroll
         for (int k = 0; k < CR_ROWS; ++k) {
             if (i0 + k < nrows) {
-                const uint32_t by = (rb[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                bits |= (by & 0x80u) ? (1u << k) : 0u;
-                const uint32_t c = by & 7u;
+                bits |= fl[k] != 0 ? (1u << k) : 0u;
+                const uint32_t c = (uint32_t)work_class(wk[k]);
                 cls |= (uint64_t)c << (4 * k);
                 ccnt += 1ull << (8 * c);
             }
@@ -192,7 +200,11 @@ hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t
 hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows, int32_t *n_ovf,
                                int32_t *order, hipStream_t s)
 {
-    compact_rows_kernel<<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
+    const bool vec = ((reinterpret_cast<uintptr_t>(row_ovf) | reinterpret_cast<uintptr_t>(order)) & 15u) == 0;
+    if (vec)
+        compact_rows_kernel<true><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
+    else
+        compact_rows_kernel<false><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
     return hipGetLastError();
 }
 
@@ -213,6 +225,12 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #endif
 #ifndef DN_PER_CU
 #define DN_PER_CU 1
+#endif
+#ifndef DU_STAGES
+#define DU_STAGES 3
+#endif
+#ifndef DU_PER_CU
+#define DU_PER_CU 1
 #endif
 #ifndef DN_KB
 #define DN_KB 128
@@ -269,6 +287,51 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dense_epi_kernel(G
                             store_elem(o.out + off, v > 0.f ? v : 0.f);
                         else
                             store_elem(o.out + off, load_elem(o.gate + off) * v);
+                    }
+                }
+    }
+}
+
+// Dense backup and gated up product of the overflow rows in one GEMM: the
+// workgroup's B tile interleaves 64-row blocks of W_g^T and W_u^T (the core's
+// dual mode), so for each of its BN/2 output columns a lane holds both
+// z = x . W_g and u = x . W_u.  Writes dense = round(ReLU(z)) and
+// prod = round(dense * u): the values of dense_epi_kernel's two modes, with
+// the same accumulation order, from one pass over A.  Same tile loop.
+template <typename TI> struct DualOut {
+    TI *dense;  // [max_ovf][N]
+    TI *prod;   // [max_ovf][N]
+};
+
+template <typename TI, int BM, int BN, int WM>
+__global__ __launch_bounds__((BM / WM) * (BN / 128) * 64) void dual_epi_kernel(GemmArgs p, DualOut<TI> o)
+{
+    using Core = GemmCore<TI, BM, BN, WM, 128, false, HB_KB, DU_STAGES, true>;
+    __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
+    const int m_used = rows_used(p);
+    const int ntiles = (m_used + BM - 1) / BM * p.NT;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / Core::NWN, wn = wave % Core::NWN;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int nt = t % p.NT, mt = t / p.NT;
+        const int m0 = mt * BM, n0 = nt * (BN / 2);
+        Core core;
+        f32x16 acc[Core::FM][Core::FN];
+        core.run(p, smem, m0, n0, m_used, p.k_begin, p.k_len, tid, acc);
+#pragma unroll
+        for (int fm = 0; fm < Core::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
+                    const int n = n0 + wn * 64 + fn * 32 + (lane & 31);
+                    if (m < m_used && n < p.N) {
+                        const int64_t off = (int64_t)m * p.N + n;
+                        const float z = acc[fm][fn][i];
+                        const TI hv = (TI)(z > 0.f ? z : 0.f);
+                        o.dense[off] = hv;
+                        store_elem(o.prod + off, (float)hv * acc[fm][fn + 2][i]);
                     }
                 }
     }
@@ -348,6 +411,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 // CU), split over K.
 constexpr int HB_BM = 64, HB_WM = 32;
 constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32, DN_WN = 128;
+// Dual gate / up GEMM: 64 rows x 128 output columns per workgroup (a 256-row
+// B tile), 4 waves of 32 x 128, 3-deep ring of 40 KiB stages (120 KiB).
+constexpr int DU_BM = 64, DU_BN = 256, DU_WM = 32;
 
 // Workgroups for a tile loop: one per CU, at most `tiles`, rounded down to a
 // multiple of 8 when that many (keeps N columns on one XCD).
@@ -405,6 +471,43 @@ hipError_t launch_gated_up(int vdtype, const void *x, int T, const void *wu_t, c
     if (vdtype == 1)
         return dense_go<__bf16, 1>(x, T, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
     return dense_go<float, 1>(x, T, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
+}
+
+template <typename TI>
+static hipError_t dual_go(const void *x, int T, const void *wg_t, const void *wu_t, const int32_t *ovf_rows,
+                          const int32_t *n_ovf, int max_ovf, int d, int F, void *dense, void *prod, hipStream_t s)
+{
+    if (max_ovf == 0)
+        return hipSuccess;
+    GemmArgs p{};
+    p.A = x;
+    p.lda = d;
+    p.a_rows = ovf_rows;
+    p.M = max_ovf;
+    p.m_count = n_ovf;
+    p.B = wg_t;
+    p.B2 = wu_t;
+    p.ldb = d;
+    p.N = F;
+    p.k_begin = 0;
+    p.k_len = d;
+    p.MT = (max_ovf + DU_BM - 1) / DU_BM;
+    p.NT = (F + DU_BN / 2 - 1) / (DU_BN / 2);
+    p.a_bytes = (uint32_t)((int64_t)T * d * sizeof(TI));
+    p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
+    DualOut<TI> o{static_cast<TI *>(dense), static_cast<TI *>(prod)};
+    dual_epi_kernel<TI, DU_BM, DU_BN, DU_WM>
+        <<<dim3(loop_grid((long)p.MT * p.NT, DU_PER_CU)), dim3((DU_BM / DU_WM) * (DU_BN / 128) * 64), 0, s>>>(p, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_gate_up(int vdtype, const void *x, int T, const void *wg_t, const void *wu_t,
+                                const int32_t *ovf_rows, const int32_t *n_ovf, int max_ovf, int d, int F, void *dense,
+                                void *pbuf, hipStream_t s)
+{
+    if (vdtype == 1)
+        return dual_go<__bf16>(x, T, wg_t, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
+    return dual_go<float>(x, T, wg_t, wu_t, ovf_rows, n_ovf, max_ovf, d, F, dense, pbuf, s);
 }
 
 int down_splits(int max_ovf, int F, int d)

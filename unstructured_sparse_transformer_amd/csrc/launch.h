@@ -39,6 +39,13 @@ hipError_t launch_gated_up(int vdtype, const void *x, int T, const void *wu_t, c
                            const int32_t *n_ovf, int max_ovf, int d, int F, const void *dense, void *p,
                            hipStream_t s);
 
+// Both of the above in one GEMM (one pass over the gathered x rows):
+// dense[i][:] = ReLU(x[ovf_rows[i]] . W_g) and p[i][:] = round(dense[i][:] *
+// (x[ovf_rows[i]] . W_u)) for i < min(*n_ovf, max_ovf); the same values.
+hipError_t launch_dense_gate_up(int vdtype, const void *x, int T, const void *wg_t, const void *wu_t,
+                                const int32_t *ovf_rows, const int32_t *n_ovf, int max_ovf, int d, int F, void *dense,
+                                void *p, hipStream_t s);
+
 // y[ovf_rows[i]][:] = p[i][:] . W_d for i < min(*n_ovf, max_ovf); split-K with
 // `splits` fp32 partial slabs in `part` ([splits][max_ovf][d]) when splits > 1.
 hipError_t launch_down(int vdtype, const void *p, const void *wd, const int32_t *ovf_rows, const int32_t *n_ovf,

@@ -106,6 +106,10 @@ __device__ __forceinline__ void tile_coords(int g, int MT, int NT, int &mt, int 
 // A rows are K-contiguous (optionally gathered through a_rows).  B is either
 // "NK" (B^T stored [N][K], K-contiguous: W_g^T, W_u^T) or "KN" ([K][N],
 // N-contiguous: W_d), the latter transposed inside LDS stage by stage.
+// Dual NK mode: two B matrices of the same shape (B, B2) share the A tile;
+// the B tile's rows alternate between them in blocks of 64 (rows 128 q + r,
+// r < 64, are B's column 64 q + r; rows 128 q + 64 + r are B2's), so a wave
+// whose tile is 128 rows wide holds both products of the same 64 columns.
 struct GemmArgs {
     const void *A;
     int64_t lda;             // elements
@@ -119,6 +123,7 @@ struct GemmArgs {
     int k_split_len;         // split-K: workgroup z-slice s covers [k_begin + s*k_split_len, +k_split_len)
     int MT, NT;              // tile grid
     uint32_t a_bytes, b_bytes;  // extents of A and B (each below 4 GiB)
+    const void *B2;          // dual mode: second B, same ldb and extent as B
 };
 
 // Buffer resource over one matrix (raw, stride 0): word 3 as CDNA3/CDNA4
@@ -148,7 +153,7 @@ __device__ __forceinline__ void wg_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <typename TI, int BM, int BN, int WM, int WN, bool B_KN, int KB = 128, int STAGES = 2>
+template <typename TI, int BM, int BN, int WM, int WN, bool B_KN, int KB = 128, int STAGES = 2, bool DUALB = false>
 struct GemmCore {
     static constexpr int NWM = BM / WM, NWN = BN / WN;
     static constexpr int NW = NWM * NWN;
@@ -182,6 +187,8 @@ struct GemmCore {
     static_assert(!B_KN || B_UNITS % NTHR == 0 || B_UNITS < NTHR, "transpose blocks split over the threads");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(!B_KN || KB == 128, "the transposed B tile's swizzle assumes 128-byte rows");
+    static_assert(!DUALB || (!B_KN && BN % 128 == 0 && WN == 128 && 64 % RPC == 0),
+                  "dual B: 64-row blocks, each wave spans one block of each matrix");
 
     // LDS byte offset of (row, 16-byte chunk) in the B operand tile.  NK: the
     // copy layout.  KN (written by transpose_b): the chunk is XOR-ed with bits
@@ -196,7 +203,7 @@ struct GemmCore {
             return lds_off<KB>(row, chunk);
     }
 
-    __amdgpu_buffer_rsrc_t ra, rb;
+    __amdgpu_buffer_rsrc_t ra, rb, rb2;
     int a_voff[A_LD];
     int b_voff[B_LD > 0 ? B_LD : 1];
     int wave;
@@ -212,6 +219,8 @@ struct GemmCore {
         constexpr int RPW_LOG = KB == 128 ? 1 : 2;
         ra = make_rsrc(p.A, p.a_bytes);
         rb = make_rsrc(p.B, p.b_bytes);
+        if constexpr (DUALB)
+            rb2 = make_rsrc(p.B2, p.b_bytes);
 #pragma unroll
         for (int j = 0; j < A_LD; ++j) {
             const int r = (j * NW + wave) * RPC + lane / CPR;
@@ -226,7 +235,7 @@ struct GemmCore {
             for (int j = 0; j < B_LD; ++j) {
                 const int r = (j * NW + wave) * RPC + lane / CPR;
                 const int c = (lane % CPR) ^ ((r >> RPW_LOG) & (CPR - 1));
-                int gn = n0 + r;
+                int gn = DUALB ? n0 + ((r >> 7) << 6) + (r & 63) : n0 + r;
                 gn = gn < p.N ? gn : p.N - 1;
                 b_voff[j] = (int)(((int64_t)gn * p.ldb + kb) * SZ + c * 16);
             }
@@ -251,7 +260,16 @@ struct GemmCore {
 #pragma unroll
         for (int j = 0; j < A_LD; ++j)
             dma16(ra, sa + (j * NW + wave) * 1024, a_voff[j], koff);
-        if constexpr (!B_KN) {
+        if constexpr (DUALB) {
+#pragma unroll
+            for (int j = 0; j < B_LD; ++j) {
+                // the copy's RPC rows lie in one 64-row block: bit 6 of its first row picks the matrix
+                if ((((j * NW + wave) * RPC) >> 6) & 1)
+                    dma16(rb2, sb + (j * NW + wave) * 1024, b_voff[j], koff);
+                else
+                    dma16(rb, sb + (j * NW + wave) * 1024, b_voff[j], koff);
+            }
+        } else if constexpr (!B_KN) {
 #pragma unroll
             for (int j = 0; j < B_LD; ++j)
                 dma16(rb, sb + (j * NW + wave) * 1024, b_voff[j], koff);
