@@ -13,9 +13,10 @@
 // elements (l + 64c)*E .. +E, so every weight-row read is one fully coalesced
 // 16-byte-per-lane sweep).  The token's TwELL entries are compacted into an LDS
 // list of (j, h) in ascending j (wave prefix sum over the per-tile counts) and
-// dealt to the waves G at a time, so heavy tokens (hundreds of entries) run 4
-// latency chains in parallel; 2*G weight rows are in flight per wave, the G
-// dot products are reduced with DPP, and y += (h*u) * W_d[j] runs in fp32.
+// dealt to the waves G at a time (G = 1), so heavy tokens (hundreds of
+// entries) run 4 latency chains in parallel; the next group's 2*G weight rows
+// are in flight while a wave reduces the current one, the dot products are
+// reduced with DPP, and y += (h*u) * W_d[j] runs in fp32.
 // The partial rows are added in LDS in a fixed order: no atomics, and the
 // result does not depend on timing.
 #include "decode.h"
@@ -23,8 +24,11 @@
 #include "twell_device.h"
 #include "wave_ops.h"
 
+// Entries per group (G).  One entry per group keeps the 2B-shaped kernel at
+// 166 VGPRs: three waves per SIMD, three tokens per CU in flight (two at
+// G = 2, 234 VGPRs), which the latency-bound light and empty rows need.
 #ifndef FUSED_G
-#define FUSED_G 2
+#define FUSED_G 1
 #endif
 
 namespace twell {
@@ -33,6 +37,18 @@ namespace twell {
 #define FUSED_WAVES 4
 #endif
 constexpr int NWV = FUSED_WAVES;  // waves per token
+
+// The token's x row as this lane's chunks in fp32 registers.
+template <typename TI, int NC> struct XRow {
+    float f[NC][Elt<TI>::PER_CHUNK];
+    __device__ __forceinline__ void set(int c, const u32x4 &v)
+    {
+#pragma unroll
+        for (int e = 0; e < Elt<TI>::PER_CHUNK; ++e)
+            f[c][e] = chunk_elem<TI>(v, e);
+    }
+    __device__ __forceinline__ float get(int c, int e) const { return f[c][e]; }
+};
 
 template <typename TI> struct FusedArgs {
     const int32_t *cnt;
@@ -74,22 +90,23 @@ __device__ __forceinline__ void group_load(const FusedArgs<TI> &a, const int2 *l
 }
 
 // y += (h * (x . W_u^T[j])) * W_d[j] for the entries of a loaded group.
+// Each dot product sums over chunks, then elements, in order.
 template <typename TI, int NC, int G>
-__device__ __forceinline__ void group_apply(const Group<TI, NC, G> &g, const float (&xf)[NC][Elt<TI>::PER_CHUNK],
+__device__ __forceinline__ void group_apply(const Group<TI, NC, G> &g, const XRow<TI, NC> &xr,
                                             float (&yacc)[NC][Elt<TI>::PER_CHUNK])
 {
     constexpr int E = Elt<TI>::PER_CHUNK;
     float part[G];
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
-        float s = 0.f;
+    for (int k = 0; k < G; ++k)
+        part[k] = 0.f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < G; ++k)
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                s = fmaf(xf[c][e], chunk_elem<TI>(g.wu[k][c], e), s);
-        part[k] = s;
-    }
+                part[k] = fmaf(xr.get(c, e), chunk_elem<TI>(g.wu[k][c], e), part[k]);
 #pragma unroll
     for (int k = 0; k < G; ++k)
         part[k] = wave_sum(part[k]);
@@ -108,7 +125,7 @@ __device__ __forceinline__ void group_apply(const Group<TI, NC, G> &g, const flo
 // group's rows requested before the current group is reduced.
 template <typename TI, int NC, int G>
 __device__ __forceinline__ void group_stream(const FusedArgs<TI> &a, const int2 *list, int q0, int step, int ngroups,
-                                             int lane, int64_t row_bytes, const float (&xf)[NC][Elt<TI>::PER_CHUNK],
+                                             int lane, int64_t row_bytes, const XRow<TI, NC> &xf,
                                              float (&yacc)[NC][Elt<TI>::PER_CHUNK])
 {
     Group<TI, NC, G> ga, gb;
@@ -172,17 +189,18 @@ __global__ __launch_bounds__(64 * NWV) void ffn_fused_kernel(FusedArgs<TI> a)
         return;
     }
 
-    float xf[NC][E], yacc[NC][E];
+    XRow<TI, NC> xf;
+    float yacc[NC][E];
     const char *xrow = (const char *)a.x + (int64_t)t * row_bytes;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            yacc[c][e] = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int ch = lane + 64 * c;
-        const u32x4 v = ch < a.nchunks ? ldg16(xrow + ch * 16) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            xf[c][e] = chunk_elem<TI>(v, e);
-            yacc[c][e] = 0.f;
-        }
+        xf.set(c, ch < a.nchunks ? ldg16(xrow + ch * 16) : u32x4{0, 0, 0, 0});
     }
 
     // This wave's tiles: b = wave + NWV * l for l = 0, 1, ...; lane l holds tile l.
@@ -407,21 +425,21 @@ __global__ __launch_bounds__(256) void ffn_chunks_kernel(ChunkArgs a)
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's list stores are done
         __builtin_amdgcn_wave_barrier();
 
-        float xf[NC][E], yacc[NC][E];
+        XRow<__bf16, NC> xf;
+        float yacc[NC][E];
         const char *xrow = (const char *)a.f.x + (int64_t)t * row_bytes;
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
             const int ch = lane + 64 * cc;
-            const u32x4 v = ch < a.f.nchunks ? ldg16(xrow + ch * 16) : u32x4{0, 0, 0, 0};
+            xf.set(cc, ch < a.f.nchunks ? ldg16(xrow + ch * 16) : u32x4{0, 0, 0, 0});
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                xf[cc][e] = chunk_elem<__bf16>(v, e);
+            for (int e = 0; e < E; ++e)
                 yacc[cc][e] = 0.f;
-            }
         }
-        const int ngroups = n / FUSED_G;
-        group_stream<__bf16, NC, FUSED_G>(a.f, list, 0, 1, ngroups, lane, row_bytes, xf, yacc);
-        for (int e0 = ngroups * FUSED_G; e0 < n; ++e0) {
+        constexpr int DG = 2;  // entries per group
+        const int ngroups = n / DG;
+        group_stream<__bf16, NC, DG>(a.f, list, 0, 1, ngroups, lane, row_bytes, xf, yacc);
+        for (int e0 = ngroups * DG; e0 < n; ++e0) {
             Group<__bf16, NC, 1> g1;
             group_load<__bf16, NC, 1>(a.f, list, e0, lane, row_bytes, g1);
             group_apply<__bf16, NC, 1>(g1, xf, yacc);

@@ -224,7 +224,7 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define HB_PER_CU 2
 #endif
 #ifndef DN_PER_CU
-#define DN_PER_CU 1
+#define DN_PER_CU 2
 #endif
 #ifndef DU_STAGES
 #define DU_STAGES 3
@@ -236,7 +236,7 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define DN_KB 128
 #endif
 #ifndef DN_STAGES
-#define DN_STAGES 3
+#define DN_STAGES 2
 #endif
 
 // ------------------------------------------------------------------ dense GEMMs
@@ -407,13 +407,23 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 // they stream whole weight matrices, so each workgroup keeps several K stages
 // of copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 3-deep
 // ring of 128-byte K stages (72 KiB), two workgroups per CU; down: 64 x 256,
-// 4 waves, 3-deep ring with the W_d stage transposed in LDS (152 KiB, one per
-// CU), split over K.
+// 8 waves of 32 x 64, 2-deep ring of raw W_d stages (bf16: read with
+// transposing LDS reads, 80 KiB; fp32: transposed in LDS, 112 KiB), split
+// over K, two workgroups per CU where they fit.
 constexpr int HB_BM = 64, HB_WM = 32;
-constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32, DN_WN = 128;
+#ifndef DN_WN
+#define DN_WN 64
+#endif
+#ifndef DN_MAX_SPLITS
+#define DN_MAX_SPLITS 8
+#endif
+constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32;
 // Dual gate / up GEMM: 64 rows x 128 output columns per workgroup (a 256-row
 // B tile), 4 waves of 32 x 128, 3-deep ring of 40 KiB stages (120 KiB).
-constexpr int DU_BM = 64, DU_BN = 256, DU_WM = 32;
+#ifndef DU_BM
+#define DU_BM 64
+#endif
+constexpr int DU_BN = 256, DU_WM = 32;
 
 // Workgroups for a tile loop: one per CU, at most `tiles`, rounded down to a
 // multiple of 8 when that many (keeps N columns on one XCD).
@@ -517,7 +527,7 @@ int down_splits(int max_ovf, int F, int d)
     // ones cover the chip.  K slices stay whole multiples of 64 elements.
     const long tiles = (long)((max_ovf + DN_BM - 1) / DN_BM) * ((d + DN_BN - 1) / DN_BN);
     int s = 1;
-    while (s < 8 && tiles * s < 2048 && F % (s * 2 * 64) == 0)
+    while (s < DN_MAX_SPLITS && tiles * s < 2048 && F % (s * 2 * 64) == 0)
         s *= 2;
     return s;
 }

@@ -168,9 +168,12 @@ struct GemmCore {
     static constexpr int LDS_A = BM * KB, LDS_B = BN * KB;
     // K-contiguous ("NK") operands arrive by global->LDS copies of 1 KiB per
     // wave instruction (RPC whole operand rows).  A KN-layout B ([K][N],
-    // N-contiguous) arrives the same way as raw [KT][BN] rows and is transposed
-    // inside LDS, 8 x 8 (bf16) or 4 x 4 (fp32) blocks at a time, into the
-    // operand layout before the stage's MFMAs.
+    // N-contiguous) arrives the same way as raw [KT][BN] rows.  bf16 (B_TR):
+    // the MFMA fragments are read from the raw rows with gfx950's transposing
+    // LDS reads (ds_read_b64_tr_b16), the raw rows' 16-byte chunks XOR-swizzled
+    // on the copy side.  fp32: the stage is transposed inside LDS, 4 x 4
+    // blocks at a time, into the operand layout before the stage's MFMAs.
+    static constexpr bool B_TR = B_KN && SZ == 2;
     static constexpr int RAW_ROW = BN * SZ;              // bytes of one raw B row
     static constexpr int B_RAW = B_KN ? KT * RAW_ROW : 0;
     static constexpr int RAW_RPI = B_KN ? 1024 / RAW_ROW : 1;  // raw rows per 1 KiB copy
@@ -178,7 +181,7 @@ struct GemmCore {
     static constexpr int B_LD = B_KN ? KT / RAW_RPI / NW : BN / RPC / NW;
     static constexpr int B_UNITS = B_KN ? (KT / E) * (BN / E) : 0;  // transpose blocks per stage
     static constexpr int BUF = LDS_A + (B_KN ? B_RAW : LDS_B);       // one ring slot
-    static constexpr int LDS_BYTES = STAGES * BUF + (B_KN ? LDS_B : 0);
+    static constexpr int LDS_BYTES = STAGES * BUF + (B_KN && !B_TR ? LDS_B : 0);
     static_assert(KB == 64 || KB == 128, "stage row width");
     static_assert(STAGES >= 2 && STAGES <= 8, "pipeline depth");
     static_assert((BM / RPC) % NW == 0, "A tile rows split over the waves");
@@ -187,6 +190,7 @@ struct GemmCore {
     static_assert(!B_KN || B_UNITS % NTHR == 0 || B_UNITS < NTHR, "transpose blocks split over the threads");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(!B_KN || KB == 128, "the transposed B tile's swizzle assumes 128-byte rows");
+    static_assert(!B_TR || (RAW_ROW % 256 == 0 && WN % 32 == 0), "raw rows span whole 256-byte bank windows");
     static_assert(!DUALB || (!B_KN && BN % 128 == 0 && WN == 128 && 64 % RPC == 0),
                   "dual B: 64-row blocks, each wave spans one block of each matrix");
 
@@ -202,6 +206,12 @@ struct GemmCore {
         else
             return lds_off<KB>(row, chunk);
     }
+
+    // B_TR: chunk slot of logical 16-byte chunk c in raw row r.  Rows k..k+3
+    // (k a multiple of 4) put any 4 consecutive chunks of a 256-byte window on
+    // 16 distinct slots, so the 32 lanes of a transposing read (4 rows x 64
+    // bytes) hit every bank once.
+    __device__ __forceinline__ static int raw_slot(int r, int c) { return c ^ ((r & 3) << 2); }
 
     __amdgpu_buffer_rsrc_t ra, rb, rb2;
     int a_voff[A_LD];
@@ -245,7 +255,9 @@ struct GemmCore {
 #pragma unroll
             for (int j = 0; j < B_LD; ++j) {
                 const int r = (j * NW + wave) * RAW_RPI + lane / LPR;  // k row within the stage
-                int gn = n0 + (lane % LPR) * E;
+                // the copy writes slot lane % LPR of the row: load the chunk that belongs there
+                const int c = B_TR ? raw_slot(r, lane % LPR) : lane % LPR;
+                int gn = n0 + c * E;
                 gn = gn <= p.N - E ? gn : p.N - E;  // columns past N re-read valid ones; results discarded
                 b_voff[j] = (int)(((int64_t)(kb + r) * p.ldb + gn) * SZ);
             }
@@ -398,9 +410,37 @@ struct GemmCore {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
             af[fm] = *reinterpret_cast<const u32x4 *>(sa + lds_off<KB>(wm * WM + fm * 32 + lr, ss * 2 + lh));
+        if constexpr (B_TR) {
+            // Lane l needs B(k0 + e, n) for e < 8, n = its column (l % 32), k0 =
+            // 16 ss + 8 (l / 32): the same K chunk as its A fragment.  Within a
+            // 16-lane group the transposing read hands lane i element i % 4 of
+            // the 8-byte pieces addressed by lanes i / 4 + 4 j (j < 4) as its
+            // values j: so lane p addresses row k0 + p / 4 (+ 4 for the second
+            // half), columns 4 (p % 4) .. +3 of the group's 16.
+            const int g = lane >> 4, pp = lane & 15;
+            const int kr = ss * 16 + ((g >> 1) << 3) + (pp >> 2);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            bf[fn] = *reinterpret_cast<const u32x4 *>(sb + b_off(wn * WN + fn * 32 + lr, ss * 2 + lh));
+            for (int fn = 0; fn < FN; ++fn) {
+                const int n = wn * WN + fn * 32 + ((g & 1) << 4) + ((pp & 3) << 2);
+                typedef short v4s __attribute__((ext_vector_type(4)));
+                v4s h[2];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int r = kr + 4 * half;
+                    const char *pa = sb + r * RAW_ROW + (raw_slot(r, n >> 3) << 4) + (((n >> 2) & 1) << 3);
+                    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(pa));
+                }
+                bf[fn] = u32x4{(uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16),
+                               (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16),
+                               (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16),
+                               (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16)};
+            }
+        } else {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                bf[fn] = *reinterpret_cast<const u32x4 *>(sb + b_off(wn * WN + fn * 32 + lr, ss * 2 + lh));
+        }
     }
     __device__ __forceinline__ static void mfma_sub(const u32x4 (&af)[FM], const u32x4 (&bf)[FN],
                                                     f32x16 (&acc)[FM][FN])
@@ -421,7 +461,7 @@ struct GemmCore {
     __device__ __forceinline__ void run_nk(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb,
                                            int klen, int tid, f32x16 (&acc)[FM][FN])
     {
-        static_assert(!B_KN && SUB % 2 == 0, "fragment buffers alternate within a stage");
+        static_assert((!B_KN || B_TR) && SUB % 2 == 0, "fragment buffers alternate within a stage");
         const int lane = tid & 63;
         const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm = wv / NWN, wn = wv % NWN;
@@ -485,7 +525,7 @@ struct GemmCore {
     __device__ __forceinline__ void run(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb, int klen,
                                         int tid, f32x16 (&acc)[FM][FN])
     {
-        if constexpr (!B_KN) {
+        if constexpr (!B_KN || B_TR) {
             run_nk(p, smem, m0, n0, m_used, kb, klen, tid, acc);
             return;
         }
