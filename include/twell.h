@@ -165,7 +165,9 @@ TWELL_API int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d,
 TWELL_API int twell_ffn_fused(const twell_t *h, const int32_t *order, const void *x, const void *wu_t,
                     const void *wd, int32_t d, float *y, void *stream);
 
-/* Bytes of device workspace twell_ffn_hybrid needs for these sizes. */
+/* Bytes of device workspace twell_ffn_hybrid, twell_ffn_overflow,
+ * twell_ffn_forward and twell_ffn_from_gate need for these sizes (0 when
+ * max_ovf is 0). */
 TWELL_API size_t twell_ffn_hybrid_workspace_bytes(int32_t max_ovf, int32_t F, int32_t d, int32_t vdtype);
 
 /* Dense part of the hybrid FFN (section 2.3 of the page): for the first

@@ -116,3 +116,36 @@ def test_stats_layer_2b_dead_neurons(gpu_lib):
     say(f"case stats layer_2b T={wl.T} d={wl.d} F={wl.F} (full oracle)")
     cnt = _check(wl, label="2b")
     assert (cnt[wl.meta["dead"]] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "0p5b"])
+def test_stats_gate_then_from_gate(gpu_lib, name):
+    """twell_pack_gate_stats followed by twell_ffn_from_gate writes the same
+    hybrid and y bits as twell_ffn_forward (the statistics change nothing else)."""
+    import torch
+    import unstructured_sparse_transformer_amd as tw
+    wl = make_tiny() if name == "tiny" else make_layer_0p5b()
+    say(f"case stats gate + twell_ffn_from_gate {wl.name}")
+    dt, x, wg, wu, wd = to_device(wl)
+    max_ovf = min(wl.T, 256)
+    n_b = wl.F // wl.tile_w
+    out = []
+    for with_stats in (False, True):
+        hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
+        y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+        ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt)
+        if with_stats:
+            ncnt = torch.zeros(wl.F, dtype=torch.int32, device="cuda")
+            l1 = torch.empty((wl.T, n_b), dtype=torch.float32, device="cuda")
+            tw.twell_pack_gate_stats(x, wg, hy.ell, ncnt, l1)
+            tw.twell_ffn_from_gate(x, wg, wu, wd, hy, y, ws)
+        else:
+            tw.twell_ffn_forward(x, wg, wu, wd, hy, y, ws)
+        torch.cuda.synchronize()
+        m = min(int(hy.n_ovf.item()), max_ovf)
+        out.append([hy.ell.cnt, hy.ell.idx, hy.ell.val.view(torch.uint8) if dt == torch.bfloat16 else hy.ell.val,
+                    hy.row_ovf, hy.n_ovf, hy.order, hy.ovf_rows[:m], hy.dense[:m].contiguous().view(torch.uint8),
+                    y.view(torch.int32)])
+    for a, b in zip(*out):
+        assert torch.equal(a, b), f"{wl.name}: stats gate + from_gate differs from twell_ffn_forward"
+    assert int(ncnt.sum().item()) == int((hy.ell.cnt.sum()).item()), f"{wl.name}: neuron counts vs TwELL counts"
