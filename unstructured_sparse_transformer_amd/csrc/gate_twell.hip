@@ -282,10 +282,10 @@ __device__ __forceinline__ void twell_epilogue(f32x16 (&acc)[WM / 32][WN / 32], 
 //           tile-local column into the segment's staging slots; the
 //           segments' true counts go to LDS.  All-zero ballots (most of them)
 //           skip the rest.
-//   pass B (one thread per (row, tile)): the tile's segments are joined in
-//           column order (the true count is their sum), and the first `cap`
-//           slots go out with 16-byte stores, slots past min(count, cap) as
-//           zeros.
+//   pass B (one thread per 8 slots of a (row, tile)): the tile's segments
+//           are joined in column order (the true count is their sum), and the
+//           first `cap` slots go out with 16-byte value and 8-byte index
+//           stores, slots past min(count, cap) as zeros.
 template <typename TI, int BN, int WN, int TW> struct SegShape {
     static constexpr int SEGW = TW < WN ? TW : WN;  // columns of a segment
     static constexpr int NSEG = BN / SEGW;          // segments per row
@@ -379,11 +379,16 @@ __device__ __forceinline__ void twell_epilogue_seg(f32x16 (&acc)[WM / 32][WN / 3
     }
     __syncthreads();
 
-    // pass B
-    const bool vec = (cap * SZ) % 16 == 0 && cap % 16 == 0 && (reinterpret_cast<uintptr_t>(o.val) & 15u) == 0 &&
-                     (reinterpret_cast<uintptr_t>(o.idx) & 15u) == 0;
-    for (int e = tid; e < BM * TPW; e += NTHR) {
-        const int r = e / TPW, tl = e - r * TPW;
+    // pass B: 8-slot units, so that every thread has a unit (two per (row,
+    // tile) at cap 16) and each unit goes out as one 16-byte (bf16) or two
+    // (fp32) value stores and one 8-byte index store; other capacities and
+    // unaligned buffers take one slot at a time.
+    const bool vec8 = cap % 8 == 0 && (reinterpret_cast<uintptr_t>(o.val) & 15u) == 0 &&
+                      (reinterpret_cast<uintptr_t>(o.idx) & 7u) == 0;
+    const int U = vec8 ? cap >> 3 : 1;  // units per (row, tile)
+    for (int e = tid; e < BM * TPW * U; e += NTHR) {
+        const int rt = e / U, u = e - rt * U;
+        const int r = rt / TPW, tl = rt - r * TPW;
         const int t = m0 + r;
         const int gcol = n0 + tl * TW;
         if (t >= M || gcol >= N)
@@ -393,47 +398,34 @@ __device__ __forceinline__ void twell_epilogue_seg(f32x16 (&acc)[WM / 32][WN / 3
         const int c1 = SPT == 2 ? (int)scnt[s0 + 1] : 0;
         const int total = c0 + c1;
         const int64_t ooff = (int64_t)t * o.n_b + gcol / TW;
-        o.cnt[ooff] = total;
-        const int k0 = min(c0, cap);           // slots taken from the first segment
+        if (u == 0)
+            o.cnt[ooff] = total;
+        const int k0 = min(c0, cap);  // slots taken from the first segment
         const int kept = min(total, cap);
         const W *sr0 = sw + (int64_t)s0 * cap;
-        const W *sr1 = sr0 + cap;              // second segment (SPT == 2)
+        const W *sr1 = sr0 + cap;     // second segment (SPT == 2)
         const int64_t off = ooff * cap;
-        if (vec) {
-            for (int b0 = 0; b0 < cap; b0 += 16) {
-                u32x4 iw = {0u, 0u, 0u, 0u};
-                uint32_t vb[16];
+        if (vec8) {
+            const int b0 = u * 8;
+            uint32_t vb[8], iw[2] = {0u, 0u};
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int sl = b0 + q;
-                    W w = (W)0;
-                    if (sl < k0)
-                        w = sr0[sl];
-                    else if (SPT == 2 && sl < kept)
-                        w = sr1[sl - k0];
-                    vb[q] = SW::bits(w);
-                    iw[q >> 2] |= (sl < kept ? SW::col(w) : 0u) << (8 * (q & 3));
-                }
-                *reinterpret_cast<u32x4 *>(o.idx + off + b0) = iw;
-                if constexpr (SZ == 2) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        u32x4 v;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            v[q] = vb[h * 8 + 2 * q] | (vb[h * 8 + 2 * q + 1] << 16);
-                        *reinterpret_cast<u32x4 *>(o.val + off + b0 + h * 8) = v;
-                    }
-                } else {
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        u32x4 v;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            v[q] = vb[h * 4 + q];
-                        *reinterpret_cast<u32x4 *>(o.val + off + b0 + h * 4) = v;
-                    }
-                }
+            for (int q = 0; q < 8; ++q) {
+                const int sl = b0 + q;
+                W w = (W)0;
+                if (sl < k0)
+                    w = sr0[sl];
+                else if (SPT == 2 && sl < kept)
+                    w = sr1[sl - k0];
+                vb[q] = SW::bits(w);
+                iw[q >> 2] |= (sl < kept ? SW::col(w) : 0u) << (8 * (q & 3));
+            }
+            *reinterpret_cast<uint2 *>(o.idx + off + b0) = make_uint2(iw[0], iw[1]);
+            if constexpr (SZ == 2) {
+                *reinterpret_cast<u32x4 *>(o.val + off + b0) =
+                    u32x4{vb[0] | (vb[1] << 16), vb[2] | (vb[3] << 16), vb[4] | (vb[5] << 16), vb[6] | (vb[7] << 16)};
+            } else {
+                *reinterpret_cast<u32x4 *>(o.val + off + b0) = u32x4{vb[0], vb[1], vb[2], vb[3]};
+                *reinterpret_cast<u32x4 *>(o.val + off + b0 + 4) = u32x4{vb[4], vb[5], vb[6], vb[7]};
             }
         } else {
             for (int sl = 0; sl < cap; ++sl) {
