@@ -339,13 +339,19 @@ __device__ __forceinline__ void twell_epilogue_seg(f32x16 (&acc)[WM / 32][WN / 3
         for (int i = 0; i < 16; ++i) {
             const int r = wm * WM + fm * 32 + acc_row(i, lane);
             uint32_t pre_lo = 0, pre_hi = 0;
+            // all FN ballots first, so that each scalar test below reads a mask
+            // whose compare has long finished
+            uint64_t bal[FN];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                bal[fn] = __ballot(acc[fm][fn][i] > 0.f);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 if (fn % BPS == 0)
                     pre_lo = pre_hi = 0;
                 const float v = acc[fm][fn][i];
                 const bool act = v > 0.f;
-                const uint64_t b = __ballot(act);
+                const uint64_t b = bal[fn];
                 const uint32_t blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
                 if (b != 0u) {
                     // pre + active lanes of this row below the lane: mbcnt counts the
