@@ -93,10 +93,6 @@ size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
     return (b + 255) & ~(size_t)255;
 }
 
-}  // namespace
-
-namespace {
-
 // Checks shared by twell_ffn_from_gate and twell_ffn_forward (T > 0).
 int check_layer(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
                 const twell_hybrid_t *hy, const float *y, const void *workspace, size_t workspace_bytes)

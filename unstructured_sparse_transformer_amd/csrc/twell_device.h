@@ -105,7 +105,8 @@ __device__ __forceinline__ void tile_coords(int g, int MT, int NT, int &mt, int 
 // C[m][n] = sum_k A[m][k] * B(k, n) over k in [k_begin, k_begin + k_len).
 // A rows are K-contiguous (optionally gathered through a_rows).  B is either
 // "NK" (B^T stored [N][K], K-contiguous: W_g^T, W_u^T) or "KN" ([K][N],
-// N-contiguous: W_d), the latter transposed inside LDS stage by stage.
+// N-contiguous: W_d), the latter read from its raw rows with transposing LDS
+// reads (bf16) or transposed inside LDS stage by stage (fp32).
 // Dual NK mode: two B matrices of the same shape (B, B2) share the A tile;
 // the B tile's rows alternate between them in blocks of 64 (rows 128 q + r,
 // r < 64, are B's column 64 q + r; rows 128 q + 64 + r are B2's), so a wave
@@ -195,7 +196,7 @@ struct GemmCore {
                   "dual B: 64-row blocks, each wave spans one block of each matrix");
 
     // LDS byte offset of (row, 16-byte chunk) in the B operand tile.  NK: the
-    // copy layout.  KN (written by transpose_b): the chunk is XOR-ed with bits
+    // copy layout.  KN, fp32 (written by transpose_b): the chunk is XOR-ed with bits
     // 1-3 of the row and bits 4-6, so that both the fragment reads (16
     // consecutive rows) and the transposing stores (rows 8 apart, both
     // parities) of a 16-lane phase hit 16 distinct 16-byte bank groups.
@@ -293,11 +294,11 @@ struct GemmCore {
         }
     }
 
-    // KN: raw [KT][BN] rows of slot `buf` -> operand layout in `bop`.
+    // KN, fp32: raw [KT][BN] rows of slot `buf` -> operand layout in `bop`.
     // Thread u handles the E x E block at k-group u / (BN/E), n-group u % (BN/E).
     __device__ __forceinline__ void transpose_b(const char *buf, char *bop, int tid)
     {
-        if constexpr (B_KN) {
+        if constexpr (B_KN && !B_TR) {
             const char *raw = buf + LDS_A;
 #pragma unroll
             for (int u0 = 0; u0 < B_UNITS; u0 += NTHR) {
@@ -311,22 +312,10 @@ struct GemmCore {
                     rr[e] = *reinterpret_cast<const u32x4 *>(raw + (kg * E + e) * RAW_ROW + ng * 16);
                 u32x4 o[E];  // o[n]: column n of the block, its E k values
 #pragma unroll
-                for (int n = 0; n < E; ++n) {
-                    if constexpr (SZ == 2) {
+                for (int n = 0; n < E; ++n)
 #pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            const uint32_t lo = rr[2 * w][n >> 1];
-                            const uint32_t hi = rr[2 * w + 1][n >> 1];
-                            const uint32_t l16 = (n & 1) ? (lo >> 16) : (lo & 0xFFFFu);
-                            const uint32_t h16 = (n & 1) ? (hi >> 16) : (hi & 0xFFFFu);
-                            o[n][w] = l16 | (h16 << 16);
-                        }
-                    } else {
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            o[n][w] = rr[w][n];
-                    }
-                }
+                    for (int w = 0; w < 4; ++w)
+                        o[n][w] = rr[w][n];
                 // Odd n-groups write their columns in the order 1, 0, 3, 2, ...:
                 // each store then covers rows of both parities, which with the
                 // B-tile swizzle puts every 16-lane phase on 16 distinct bank groups.
