@@ -505,10 +505,21 @@ __global__ __launch_bounds__(256) void chunk_reduce_kernel(const float *part, co
     const int nv = *n_ovf < max_ovf ? *n_ovf : max_ovf;
     if (i >= nv)
         return;
+    // 8 elements per thread and step (F is a multiple of 64; z rows and dense
+    // rows are 16-byte aligned), so a thread's loads are all in flight together
     const float *zr = z + (int64_t)ovf_rows[i] * F;
-    for (int j = threadIdx.x; j < F; j += 256) {
-        const float v = zr[j];
-        store_elem(dense + (int64_t)i * F + j, v > 0.f ? v : 0.f);
+    __bf16 *dr = dense + (int64_t)i * F;
+#pragma unroll 4
+    for (int j = threadIdx.x * 8; j < F; j += 256 * 8) {
+        const float4 p = *reinterpret_cast<const float4 *>(zr + j);
+        const float4 q = *reinterpret_cast<const float4 *>(zr + j + 4);
+        const float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            h[e] = __builtin_bit_cast(uint16_t, (__bf16)(v[e] > 0.f ? v[e] : 0.f));
+        *reinterpret_cast<u32x4 *>(dr + j) =
+            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
 }
 
