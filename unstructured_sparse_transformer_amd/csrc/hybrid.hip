@@ -208,6 +208,11 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
     return hipGetLastError();
 }
 
+// Compile-time tuning knobs of the small-M GEMMs (-D on the compiler line),
+// defaults as measured best at the 2B-like layer: HB_* the separate gate and
+// up GEMMs, DU_* the dual gate/up GEMM, DN_* the down GEMM (N tile width,
+// stage width in bytes, ring depth, workgroups per CU, wave tile width, most
+// K splits).  Shapes the knobs do not cover are the constants further down.
 #ifndef HB_BN
 #define HB_BN 128
 #endif
@@ -237,6 +242,15 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #endif
 #ifndef DN_STAGES
 #define DN_STAGES 2
+#endif
+#ifndef DN_WN
+#define DN_WN 64
+#endif
+#ifndef DN_MAX_SPLITS
+#define DN_MAX_SPLITS 8
+#endif
+#ifndef DU_BM
+#define DU_BM 64
 #endif
 
 // ------------------------------------------------------------------ dense GEMMs
@@ -411,18 +425,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 // transposing LDS reads, 80 KiB; fp32: transposed in LDS, 112 KiB), split
 // over K, two workgroups per CU where they fit.
 constexpr int HB_BM = 64, HB_WM = 32;
-#ifndef DN_WN
-#define DN_WN 64
-#endif
-#ifndef DN_MAX_SPLITS
-#define DN_MAX_SPLITS 8
-#endif
 constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32;
 // Dual gate / up GEMM: 64 rows x 128 output columns per workgroup (a 256-row
 // B tile), 4 waves of 32 x 128, 3-deep ring of 40 KiB stages (120 KiB).
-#ifndef DU_BM
-#define DU_BM 64
-#endif
 constexpr int DU_BN = 256, DU_WM = 32;
 
 // Workgroups for a tile loop: one per CU, at most `tiles`, rounded down to a
