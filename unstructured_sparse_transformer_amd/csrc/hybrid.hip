@@ -212,7 +212,8 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 // defaults as measured best at the 2B-like layer: HB_* the separate gate and
 // up GEMMs, DU_* the dual gate/up GEMM, DN_* the down GEMM (N tile width,
 // stage width in bytes, ring depth, workgroups per CU, wave tile width, most
-// K splits).  Shapes the knobs do not cover are the constants further down.
+// K splits; DU_DB the W_g / W_u block height, DU_BN the B tile's rows).
+// Shapes the knobs do not cover are the constants further down.
 #ifndef HB_BN
 #define HB_BN 128
 #endif
@@ -235,7 +236,7 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define DU_STAGES 3
 #endif
 #ifndef DU_PER_CU
-#define DU_PER_CU 1
+#define DU_PER_CU 2
 #endif
 #ifndef DN_KB
 #define DN_KB 128
@@ -251,6 +252,12 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #endif
 #ifndef DU_BM
 #define DU_BM 64
+#endif
+#ifndef DU_DB
+#define DU_DB 32
+#endif
+#ifndef DU_BN
+#define DU_BN 128
 #endif
 
 // ------------------------------------------------------------------ dense GEMMs
@@ -307,7 +314,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void dense_epi_kernel(G
 }
 
 // Dense backup and gated up product of the overflow rows in one GEMM: the
-// workgroup's B tile interleaves 64-row blocks of W_g^T and W_u^T (the core's
+// workgroup's B tile interleaves DB-row blocks of W_g^T and W_u^T (the core's
 // dual mode), so for each of its BN/2 output columns a lane holds both
 // z = x . W_g and u = x . W_u.  Writes dense = round(ReLU(z)) and
 // prod = round(dense * u): the values of dense_epi_kernel's two modes, with
@@ -317,10 +324,11 @@ template <typename TI> struct DualOut {
     TI *prod;   // [max_ovf][N]
 };
 
-template <typename TI, int BM, int BN, int WM>
-__global__ __launch_bounds__((BM / WM) * (BN / 128) * 64) void dual_epi_kernel(GemmArgs p, DualOut<TI> o)
+template <typename TI, int BM, int BN, int WM, int DB>
+__global__ __launch_bounds__((BM / WM) * (BN / (2 * DB)) * 64) void dual_epi_kernel(GemmArgs p, DualOut<TI> o)
 {
-    using Core = GemmCore<TI, BM, BN, WM, 128, false, HB_KB, DU_STAGES, true>;
+    using Core = GemmCore<TI, BM, BN, WM, 2 * DB, false, HB_KB, DU_STAGES, DB>;
+    constexpr int ZB = DB / 32;  // 32-column blocks of each product per wave
     __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
     const int m_used = rows_used(p);
     const int ntiles = (m_used + BM - 1) / BM * p.NT;
@@ -335,17 +343,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / 128) * 64) void dual_epi_kernel(G
 #pragma unroll
         for (int fm = 0; fm < Core::FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < 2; ++fn)
+            for (int fn = 0; fn < ZB; ++fn)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
-                    const int n = n0 + wn * 64 + fn * 32 + (lane & 31);
+                    const int n = n0 + wn * DB + fn * 32 + (lane & 31);
                     if (m < m_used && n < p.N) {
                         const int64_t off = (int64_t)m * p.N + n;
                         const float z = acc[fm][fn][i];
                         const TI hv = (TI)(z > 0.f ? z : 0.f);
                         o.dense[off] = hv;
-                        store_elem(o.prod + off, (float)hv * acc[fm][fn + 2][i]);
+                        store_elem(o.prod + off, (float)hv * acc[fm][fn + ZB][i]);
                     }
                 }
     }
@@ -426,9 +434,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 // over K, two workgroups per CU where they fit.
 constexpr int HB_BM = 64, HB_WM = 32;
 constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32;
-// Dual gate / up GEMM: 64 rows x 128 output columns per workgroup (a 256-row
-// B tile), 4 waves of 32 x 128, 3-deep ring of 40 KiB stages (120 KiB).
-constexpr int DU_BN = 256, DU_WM = 32;
+// Dual gate / up GEMM: 64 rows x 64 output columns per workgroup (a 128-row
+// B tile of 32-row W_g / W_u blocks), 4 waves of 32 x 64, 3-deep ring of
+// 24 KiB stages (72 KiB), two workgroups per CU (64-row blocks, 128 columns
+// and one 120 KiB workgroup per CU measured 2.5-12 us slower per call).
+constexpr int DU_WM = 32;
 
 // Workgroups for a tile loop: one per CU, at most `tiles`, rounded down to a
 // multiple of 8 when that many (keeps N columns on one XCD).
@@ -511,8 +521,8 @@ static hipError_t dual_go(const void *x, int T, const void *wg_t, const void *wu
     p.a_bytes = (uint32_t)((int64_t)T * d * sizeof(TI));
     p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
     DualOut<TI> o{static_cast<TI *>(dense), static_cast<TI *>(prod)};
-    dual_epi_kernel<TI, DU_BM, DU_BN, DU_WM>
-        <<<dim3(loop_grid((long)p.MT * p.NT, DU_PER_CU)), dim3((DU_BM / DU_WM) * (DU_BN / 128) * 64), 0, s>>>(p, o);
+    dual_epi_kernel<TI, DU_BM, DU_BN, DU_WM, DU_DB>
+        <<<dim3(loop_grid((long)p.MT * p.NT, DU_PER_CU)), dim3((DU_BM / DU_WM) * (DU_BN / (2 * DU_DB)) * 64), 0, s>>>(p, o);
     return hipGetLastError();
 }
 

@@ -107,10 +107,11 @@ __device__ __forceinline__ void tile_coords(int g, int MT, int NT, int &mt, int 
 // "NK" (B^T stored [N][K], K-contiguous: W_g^T, W_u^T) or "KN" ([K][N],
 // N-contiguous: W_d), the latter read from its raw rows with transposing LDS
 // reads (bf16) or transposed inside LDS stage by stage (fp32).
-// Dual NK mode: two B matrices of the same shape (B, B2) share the A tile;
-// the B tile's rows alternate between them in blocks of 64 (rows 128 q + r,
-// r < 64, are B's column 64 q + r; rows 128 q + 64 + r are B2's), so a wave
-// whose tile is 128 rows wide holds both products of the same 64 columns.
+// Dual NK mode (block size DB > 0): two B matrices of the same shape (B, B2)
+// share the A tile; the B tile's rows alternate between them in blocks of DB
+// (rows 2 DB q + r, r < DB, are B's column DB q + r; rows 2 DB q + DB + r are
+// B2's), so a wave whose tile is 2 DB rows wide holds both products of the
+// same DB columns.
 struct GemmArgs {
     const void *A;
     int64_t lda;             // elements
@@ -154,7 +155,7 @@ __device__ __forceinline__ void wg_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <typename TI, int BM, int BN, int WM, int WN, bool B_KN, int KB = 128, int STAGES = 2, bool DUALB = false>
+template <typename TI, int BM, int BN, int WM, int WN, bool B_KN, int KB = 128, int STAGES = 2, int DUALB = 0>
 struct GemmCore {
     static constexpr int NWM = BM / WM, NWN = BN / WN;
     static constexpr int NW = NWM * NWN;
@@ -192,8 +193,8 @@ struct GemmCore {
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(!B_KN || KB == 128, "the transposed B tile's swizzle assumes 128-byte rows");
     static_assert(!B_TR || (RAW_ROW % 256 == 0 && WN % 32 == 0), "raw rows span whole 256-byte bank windows");
-    static_assert(!DUALB || (!B_KN && BN % 128 == 0 && WN == 128 && 64 % RPC == 0),
-                  "dual B: 64-row blocks, each wave spans one block of each matrix");
+    static_assert(DUALB == 0 || (!B_KN && BN % (2 * DUALB) == 0 && WN == 2 * DUALB && DUALB % RPC == 0),
+                  "dual B: DUALB-row blocks, each wave spans one block of each matrix");
 
     // LDS byte offset of (row, 16-byte chunk) in the B operand tile.  NK: the
     // copy layout.  KN, fp32 (written by transpose_b): the chunk is XOR-ed with bits
@@ -230,7 +231,7 @@ struct GemmCore {
         constexpr int RPW_LOG = KB == 128 ? 1 : 2;
         ra = make_rsrc(p.A, p.a_bytes);
         rb = make_rsrc(p.B, p.b_bytes);
-        if constexpr (DUALB)
+        if constexpr (DUALB > 0)
             rb2 = make_rsrc(p.B2, p.b_bytes);
 #pragma unroll
         for (int j = 0; j < A_LD; ++j) {
@@ -246,7 +247,7 @@ struct GemmCore {
             for (int j = 0; j < B_LD; ++j) {
                 const int r = (j * NW + wave) * RPC + lane / CPR;
                 const int c = (lane % CPR) ^ ((r >> RPW_LOG) & (CPR - 1));
-                int gn = DUALB ? n0 + ((r >> 7) << 6) + (r & 63) : n0 + r;
+                int gn = DUALB > 0 ? n0 + r / (2 * DUALB) * DUALB + r % DUALB : n0 + r;
                 gn = gn < p.N ? gn : p.N - 1;
                 b_voff[j] = (int)(((int64_t)gn * p.ldb + kb) * SZ + c * 16);
             }
@@ -273,11 +274,11 @@ struct GemmCore {
 #pragma unroll
         for (int j = 0; j < A_LD; ++j)
             dma16(ra, sa + (j * NW + wave) * 1024, a_voff[j], koff);
-        if constexpr (DUALB) {
+        if constexpr (DUALB > 0) {
 #pragma unroll
             for (int j = 0; j < B_LD; ++j) {
-                // the copy's RPC rows lie in one 64-row block: bit 6 of its first row picks the matrix
-                if ((((j * NW + wave) * RPC) >> 6) & 1)
+                // the copy's RPC rows lie in one DUALB-row block, whose parity picks the matrix
+                if ((((j * NW + wave) * RPC) / DUALB) & 1)
                     dma16(rb2, sb + (j * NW + wave) * 1024, b_voff[j], koff);
                 else
                     dma16(rb, sb + (j * NW + wave) * 1024, b_voff[j], koff);
