@@ -230,7 +230,7 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define HB_PER_CU 2
 #endif
 #ifndef DN_PER_CU
-#define DN_PER_CU 2
+#define DN_PER_CU 3
 #endif
 #ifndef DU_STAGES
 #define DU_STAGES 3
@@ -246,6 +246,9 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #endif
 #ifndef DN_WN
 #define DN_WN 64
+#endif
+#ifndef DN_BN
+#define DN_BN 128
 #endif
 #ifndef DN_MAX_SPLITS
 #define DN_MAX_SPLITS 8
@@ -428,12 +431,12 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 // Small-M tile shapes for the hybrid GEMMs (M = overflow rows, a few hundred;
 // they stream whole weight matrices, so each workgroup keeps several K stages
 // of copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 3-deep
-// ring of 128-byte K stages (72 KiB), two workgroups per CU; down: 64 x 256,
-// 8 waves of 32 x 64, 2-deep ring of raw W_d stages (bf16: read with
-// transposing LDS reads, 80 KiB; fp32: transposed in LDS, 112 KiB), split
-// over K, two workgroups per CU where they fit.
+// ring of 128-byte K stages (72 KiB), two workgroups per CU; down: 64 x 128,
+// 4 waves of 32 x 64, 2-deep ring of raw W_d stages (bf16: read with
+// transposing LDS reads, 48 KiB; fp32: transposed in LDS, 64 KiB), split
+// over K, three workgroups per CU where they fit.
 constexpr int HB_BM = 64, HB_WM = 32;
-constexpr int DN_BM = 64, DN_BN = 256, DN_WM = 32;
+constexpr int DN_BM = 64, DN_WM = 32;
 // Dual gate / up GEMM: 64 rows x 64 output columns per workgroup (a 128-row
 // B tile of 32-row W_g / W_u blocks), 4 waves of 32 x 64, 3-deep ring of
 // 24 KiB stages (72 KiB), two workgroups per CU (64-row blocks, 128 columns
