@@ -416,13 +416,21 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
     if (n >= N)
         return;
     for (int m = blockIdx.y; m < m_used; m += gridDim.y) {
-        float4 acc = *reinterpret_cast<const float4 *>(part + (int64_t)m * N + n);
-        for (int s = 1; s < splits; ++s) {
-            const float4 v = *reinterpret_cast<const float4 *>(part + ((int64_t)s * M_cap + m) * N + n);
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
+        // every slab's loads first (at most DN_MAX_SPLITS), then the sum in slab order
+        float4 v[DN_MAX_SPLITS];
+#pragma unroll
+        for (int s = 0; s < DN_MAX_SPLITS; ++s)
+            v[s] = s < splits ? *reinterpret_cast<const float4 *>(part + ((int64_t)s * M_cap + m) * N + n)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 acc = v[0];
+#pragma unroll
+        for (int s = 1; s < DN_MAX_SPLITS; ++s) {
+            if (s < splits) {
+                acc.x += v[s].x;
+                acc.y += v[s].y;
+                acc.z += v[s].z;
+                acc.w += v[s].w;
+            }
         }
         *reinterpret_cast<float4 *>(y + (int64_t)rows[m] * N + n) = acc;
     }
