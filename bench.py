@@ -567,7 +567,8 @@ def energy_per_token(fns, tokens_per_call, seconds, torch):
 def run_decode(args, wl, tw, torch, np):
     """Decode-shaped calls (T <= 64, bf16): one twell_ffn_decode call per step
     (gate, packing and partition, chunked gather, reduction: 4 kernels), next
-    to the batch path (twell_ffn_forward) and the dense bf16 FFN on the same rows.
+    to the same call replayed from a HIP graph, the batch path
+    (twell_ffn_forward) and the dense bf16 FFN on the same rows.
     Roofline: the step is bound by HBM; its algorithmic bytes are W_g read
     once, the W_u / W_d rows of every active (row, neuron), x, y and the TwELL
     written."""
@@ -611,6 +612,19 @@ def run_decode(args, wl, tw, torch, np):
         tw.twell_ffn_forward(x, wg, wu, wd, hb, y, wsb)
 
     _, ms_batch = timed(batch, args.steps)
+    # the same call captured once into a HIP graph and replayed: the host's
+    # launch cost of the four kernels leaves the step
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    gms_wall, gms_ev = timed(graph.replay, args.steps)
     out = {
         "metric": METRIC, "value": round(wl.T / (ms_wall * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle_seconds,
@@ -625,6 +639,8 @@ def run_decode(args, wl, tw, torch, np):
                      "algorithmic_bytes": alg},
         "step_ms_events": round(ms_ev, 4),
         "batch_path_ms": round(ms_batch, 4),
+        "graph_replay": {"ms_per_step": round(gms_wall, 4), "ms_events": round(gms_ev, 4),
+                         "tokens_per_s": round(wl.T / (gms_wall * 1e-3), 1)},
         "workload_stats": {"nnz": nnz, "n_ovf": n_ovf},
     }
     if not args.no_dense:
