@@ -75,6 +75,8 @@ def test_pack_gate_validation():
     assert f(GOOD, GOOD, 64, ctypes.byref(_desc(vd=2)), None) == -4
     assert f(GOOD, GOOD, 8192, ctypes.byref(_desc()), None) == -4           # bf16 row > 8 KiB
     assert f(GOOD, GOOD, 4096, ctypes.byref(_desc(vd=0)), None) == -4       # f32 row > 8 KiB
+    assert f(GOOD, GOOD, 2048, ctypes.byref(_desc(T=1 << 20, F=8192, w=256, cap=16)), None) == -3  # x = 4 GiB
+    assert f(GOOD, GOOD, 64, ctypes.byref(_desc(T=1 << 15, F=1 << 16, w=32, cap=32)), None) == -3  # 2^31 slots
     assert f(None, None, 64, ctypes.byref(_desc(T=0)), None) == 0           # T = 0: nothing to do
 
 
