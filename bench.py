@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DEC_WINDOWS = 64  # decode workloads: windows of the 2B layer the steps cycle through
 METRIC = "sparse-FFN tokens/sec at 2B shape; HBM GB/s and MFMA util as % of peak"
 
 
@@ -316,7 +317,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded grid-mode inputs of the workload's shape and sparsity; no trained weights)",
-        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
+        "config": {"workload": f"decode_2b_T{wl.T} (windows 0..{nw - 1} of T tokens in turn)", "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
                    "cap": wl.cap, "max_ovf": max_ovf, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "stages_ms": {"pack_gate": round(float(main_ms[0]), 4), "ffn_from_gate": round(float(main_ms[1]), 4),
@@ -568,19 +569,29 @@ def run_decode(args, wl, tw, torch, np):
     """Decode-shaped calls (T <= 64, bf16): one twell_ffn_decode call per step
     (gate, packing and partition, chunked gather, reduction: 4 kernels), next
     to the same call replayed from a HIP graph, the batch path
-    (twell_ffn_forward) and the dense bf16 FFN on the same rows.
+    (twell_ffn_forward) and the dense bf16 FFN on the same rows.  Step i
+    takes window i mod 64 of the 2B layer's tokens (64 disjoint windows of T
+    consecutive tokens, resident in HBM), so the timed steps see the layer's
+    spread of active counts rather than one window's.
     Roofline: the step is bound by HBM; its algorithmic bytes are W_g read
     once, the W_u / W_d rows of every active (row, neuron), x, y and the TwELL
-    written."""
+    written (averaged over the windows the timed steps take)."""
+    from workloads import make_decode_windows
     dev = "cuda"
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)  # noqa: E731
-    x, wg, wu, wd = to(wl.x), to(wl.wg_t), to(wl.wu_t), to(wl.wd)
+    wins = make_decode_windows(wl.T, max_windows=DEC_WINDOWS)
+    nw = len(wins)
+    xs = to(np.concatenate([w.x for w in wins])).reshape(nw, wl.T, wl.d)
+    xv = [xs[i] for i in range(nw)]
+    wg, wu, wd = to(wl.wg_t), to(wl.wu_t), to(wl.wd)
     hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, torch.bfloat16, wl.T)
     ws = tw.decode_workspace(wl.T, wl.F, wl.d, wl.tile_w)
     y = torch.empty((wl.T, wl.d), dtype=torch.float32, device=dev)
+    cur = [0]  # the next step's window
 
     def step():
-        tw.twell_ffn_decode(x, wg, wu, wd, hy, y, ws)
+        tw.twell_ffn_decode(xv[cur[0] % nw], wg, wu, wd, hy, y, ws)
+        cur[0] += 1
 
     def timed(fn, k):
         evs = [(DevEvent(), DevEvent()) for _ in range(k)]
@@ -588,6 +599,7 @@ def run_decode(args, wl, tw, torch, np):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
+        cur[0] = 0  # the timed steps take windows 0, 1, ...
         t0 = time.perf_counter()
         for e in evs:
             e[0].record()
@@ -598,40 +610,55 @@ def run_decode(args, wl, tw, torch, np):
         return wall * 1e3 / k, float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     ms_wall, ms_ev = timed(step, args.steps)
-    n_ovf = int(hy.n_ovf.item())
-    nnz = int(hy.ell.cnt.sum().item())
+    # per-window entries and overflow rows of the windows the timed steps took
+    nnz_w, ovf_w = [], []
+    for i in range(nw):
+        tw.twell_ffn_decode(xv[i], wg, wu, wd, hy, y, ws)
+        torch.cuda.synchronize()
+        nnz_w.append(int(hy.ell.cnt.sum().item()))
+        ovf_w.append(int(hy.n_ovf.item()))
+    used = [i % nw for i in range(args.steps)]
+    nnz = float(np.mean([nnz_w[i] for i in used]))
     esz = 2
     n_b = wl.F // wl.tile_w
-    alg = (wl.F * wl.d * esz + wl.T * wl.d * esz + nnz * 2 * wl.d * esz + wl.T * wl.d * 4 +
-           wl.T * n_b * (4 + wl.cap * (esz + 1)))
+    alg = int(wl.F * wl.d * esz + wl.T * wl.d * esz + nnz * 2 * wl.d * esz + wl.T * wl.d * 4 +
+              wl.T * n_b * (4 + wl.cap * (esz + 1)))
     # the batch path on the same rows
     hb = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, torch.bfloat16, wl.T)
     wsb = tw.hybrid_workspace(wl.T, wl.F, wl.d, torch.bfloat16)
 
     def batch():
-        tw.twell_ffn_forward(x, wg, wu, wd, hb, y, wsb)
+        tw.twell_ffn_forward(xv[cur[0] % nw], wg, wu, wd, hb, y, wsb)
+        cur[0] += 1
 
     _, ms_batch = timed(batch, args.steps)
-    # the same call captured once into a HIP graph and replayed: the host's
-    # launch cost of the four kernels leaves the step
+    # the same calls captured into HIP graphs (one per window) and replayed:
+    # the host's launch cost of the four kernels leaves the step
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
+    graphs = []  # one graph per window (a graph keeps the x pointer it captured)
+    for i in range(nw):
+        graphs.append(torch.cuda.CUDAGraph())
+        with torch.cuda.graph(graphs[-1]):
+            tw.twell_ffn_decode(xv[i], wg, wu, wd, hy, y, ws)
     torch.cuda.synchronize()
-    gms_wall, gms_ev = timed(graph.replay, args.steps)
+
+    def replay():
+        graphs[cur[0] % nw].replay()
+        cur[0] += 1
+
+    gms_wall, gms_ev = timed(replay, args.steps)
     out = {
         "metric": METRIC, "value": round(wl.T / (ms_wall * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle_seconds,
         "ms_per_step": round(ms_wall, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded grid-mode inputs of the workload's shape and sparsity; no trained weights)",
-        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
+        "config": {"workload": f"decode_2b_T{wl.T} (windows 0..{nw - 1} of T tokens in turn)", "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
                    "cap": wl.cap, "path": "twell_ffn_decode", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "decode step (gate, packing, gather, reduction)",
                      "achieved": round(alg / (ms_ev * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -641,11 +668,15 @@ def run_decode(args, wl, tw, torch, np):
         "batch_path_ms": round(ms_batch, 4),
         "graph_replay": {"ms_per_step": round(gms_wall, 4), "ms_events": round(gms_ev, 4),
                          "tokens_per_s": round(wl.T / (gms_wall * 1e-3), 1)},
-        "workload_stats": {"nnz": nnz, "n_ovf": n_ovf},
+        "workload_stats": {"windows": nw, "mean_nnz_timed": round(nnz, 2),
+                           "nnz_per_window_min_max": [min(nnz_w), max(nnz_w)],
+                           "windows_with_overflow": int(sum(1 for v in ovf_w if v > 0))},
     }
     if not args.no_dense:
         def dense_step():
-            h = torch.relu(torch.matmul(x, wg.t())) * torch.matmul(x, wu.t())
+            xx = xv[cur[0] % nw]
+            cur[0] += 1
+            h = torch.relu(torch.matmul(xx, wg.t())) * torch.matmul(xx, wu.t())
             return torch.matmul(h, wd)
         _, dms = timed(dense_step, args.steps)
         out["dense_bf16_ffn"] = {"ms_per_step": round(dms, 4), "sparse_speedup": round(dms / ms_ev, 3)}
