@@ -317,7 +317,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded grid-mode inputs of the workload's shape and sparsity; no trained weights)",
-        "config": {"workload": f"decode_2b_T{wl.T} (windows 0..{nw - 1} of T tokens in turn)", "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
                    "cap": wl.cap, "max_ovf": max_ovf, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "stages_ms": {"pack_gate": round(float(main_ms[0]), 4), "ffn_from_gate": round(float(main_ms[1]), 4),
