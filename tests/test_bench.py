@@ -1,6 +1,8 @@
 """bench.py's host-side contract (no GPU needed): more than one GPU is
 refused with a one-line JSON message and a non-zero exit, before anything
-touches a device."""
+touches a device; and every name that bench.py's and __graft_entry__.py's
+functions read is bound somewhere in scope (their GPU paths cannot run here,
+so a misnamed variable would otherwise surface only on the GPU)."""
 
 import json
 import os
@@ -18,3 +20,51 @@ def test_bench_refuses_several_gpus():
     assert len(lines) == 1, r.stdout
     msg = json.loads(lines[0])
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def _names_bound(fn):
+    """Every name a function (with its nested functions and lambdas) binds."""
+    import ast
+    names = set()
+    for n in ast.walk(fn):
+        if isinstance(n, ast.Name) and isinstance(n.ctx, (ast.Store, ast.Del)):
+            names.add(n.id)
+        elif isinstance(n, (ast.FunctionDef, ast.AsyncFunctionDef, ast.ClassDef)):
+            names.add(n.name)
+        elif isinstance(n, (ast.Import, ast.ImportFrom)):
+            names.update((a.asname or a.name).split(".")[0] for a in n.names)
+        elif isinstance(n, ast.ExceptHandler) and n.name:
+            names.add(n.name)
+        elif isinstance(n, ast.arg):
+            names.add(n.arg)
+    return names
+
+
+def _unbound_loads(path):
+    """Names a function reads that neither it, its enclosing scopes, the module
+    nor the builtins bind: the NameErrors that only a run on a GPU would show."""
+    import ast
+    import builtins
+    tree = ast.parse(open(path).read())
+    module = set(dir(builtins)) | {"__file__", "__name__"}
+    for st in tree.body:
+        if isinstance(st, (ast.FunctionDef, ast.AsyncFunctionDef, ast.ClassDef)):
+            module.add(st.name)
+            continue
+        for n in ast.walk(st):
+            if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Store):
+                module.add(n.id)
+            elif isinstance(n, (ast.Import, ast.ImportFrom)):
+                module.update((a.asname or a.name).split(".")[0] for a in n.names)
+    bad = []
+    for st in tree.body:
+        if isinstance(st, (ast.FunctionDef, ast.AsyncFunctionDef)):
+            ok = module | _names_bound(st)
+            bad += [f"{st.name}: {n.id} (line {n.lineno})" for n in ast.walk(st)
+                    if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Load) and n.id not in ok]
+    return bad
+
+
+def test_bench_and_entry_names_resolve():
+    for f in ("bench.py", "__graft_entry__.py"):
+        assert _unbound_loads(os.path.join(ROOT, f)) == [], f
