@@ -14,6 +14,20 @@ The functions carry the C names (``include/twell.h``):
 ``twell_hybrid_to_dense``, ``twell_compact_min_bytes``, ``twell_compact_hybrid``,
 ``twell_compact_to_dense``, ``twell_ffn_backward``,
 ``twell_ffn_backward_workspace_bytes``.
+
+One layer's forward pass, bf16 (x [T][d], W_g^T and W_u^T [F][d], W_d [F][d],
+all contiguous on the GPU; y [T][d] fp32)::
+
+    import unstructured_sparse_transformer_amd as tw
+    hy = tw.Hybrid.empty(T, F, tile_w=256, cap=16, dtype=torch.bfloat16, max_ovf=1024)
+    ws = tw.hybrid_workspace(1024, F, d, torch.bfloat16)
+    tw.twell_ffn_forward(x, wg_t, wu_t, wd, hy, y, ws)   # on the current stream
+    # hy.ell holds the TwELL of ReLU(x W_g); hy.n_ovf counts the overflow rows.
+    # Overflow rows past max_ovf are counted but not computed: after
+    # synchronising, check n_ovf <= max_ovf and grow max_ovf otherwise.
+
+For T <= 64 tokens, ``twell_ffn_decode`` with ``decode_workspace(T, F, d,
+tile_w)`` computes the same in four short kernels.
 """
 
 from __future__ import annotations
