@@ -54,9 +54,11 @@ __device__ __forceinline__ int work_class(int e)
     return e == 0 ? 0 : e < 16 ? 1 : e < 32 ? 2 : e < 64 ? 3 : e < 128 ? 4 : e < 192 ? 5 : e < 256 ? 6 : 7;
 }
 
-// One workgroup, per chunk of 16384 rows: thread i owns rows [16 i, 16 i + 16)
-// of the chunk and reads their flags and work values with one batch of
-// loads (16-byte vectors when VEC).  Nine per-thread counts (flagged rows;
+// One workgroup, per chunk of 16384 rows: thread i owns rows [ROWS i, ROWS i +
+// ROWS) of the chunk and reads their flags and work values with one batch of
+// loads (16-byte vectors when VEC).  ROWS = 16 makes a pass one chunk; when
+// all rows fit in 8192, ROWS = 8 covers them in one pass (the same single
+// chunk) with half of each thread's serial work (layer_2b: 7.9 -> 6.5 us).  Nine per-thread counts (flagged rows;
 // rows of each work class) go through one workgroup exclusive scan (DPP
 // wave scans + 16 wave totals in LDS); each thread writes its flagged rows to
 // the ascending overflow list and its rows to their places in the chunk's
@@ -65,27 +67,29 @@ __device__ __forceinline__ int work_class(int e)
 // values on entry; each chunk reads all of its values before the first
 // barrier and writes only its own positions after it.  n_ovf is the true
 // number of flagged rows.
-constexpr int CR_THREADS = 1024, CR_ROWS = 16, CR_NC = 8, CR_CHUNK = CR_THREADS * CR_ROWS;
+constexpr int CR_THREADS = 1024, CR_NC = 8, CR_CHUNK = 16384;  // rows per work-order chunk
 
-template <bool VEC>
+template <bool VEC, int ROWS>
 __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t *__restrict__ row_ovf, int T,
                                                                   int max_ovf, int32_t *__restrict__ ovf_rows,
                                                                   int32_t *__restrict__ n_ovf, int32_t *order)
 {
     constexpr int NV = CR_NC + 1;  // scanned values: classes 0..7, flagged rows
     constexpr int NW = CR_THREADS / 64;
+    constexpr int PASS = CR_THREADS * ROWS;  // rows per pass: a whole chunk, or (ROWS = 8) all T <= 8192 rows
+    static_assert(PASS == CR_CHUNK || PASS * 2 == CR_CHUNK, "a pass is a chunk, or half of one used for T <= PASS");
     __shared__ int wave_tot[NW][NV];
     __shared__ int wave_off[NW + 1][NV];  // exclusive prefix over waves; row NW = totals
-    __shared__ int sord[CR_CHUNK];        // the chunk's work order
+    __shared__ int sord[PASS];        // the chunk's work order
     const int tid = threadIdx.x, wave = tid >> 6;
     int base = 0;
-    for (int t0 = 0; t0 < T; t0 += CR_CHUNK) {
-        const int nrows = T - t0 < CR_CHUNK ? T - t0 : CR_CHUNK;
-        const int i0 = tid * CR_ROWS;
-        int fl[CR_ROWS], wk[CR_ROWS];
-        if (VEC && i0 + CR_ROWS <= nrows) {
+    for (int t0 = 0; t0 < T; t0 += PASS) {
+        const int nrows = T - t0 < PASS ? T - t0 : PASS;
+        const int i0 = tid * ROWS;
+        int fl[ROWS], wk[ROWS];
+        if (VEC && i0 + ROWS <= nrows) {
 #pragma unroll
-            for (int q = 0; q < CR_ROWS / 4; ++q) {
+            for (int q = 0; q < ROWS / 4; ++q) {
                 const int4 f4 = *reinterpret_cast<const int4 *>(row_ovf + t0 + i0 + 4 * q);
                 const int4 w4 = *reinterpret_cast<const int4 *>(order + t0 + i0 + 4 * q);
                 fl[4 * q] = f4.x, fl[4 * q + 1] = f4.y, fl[4 * q + 2] = f4.z, fl[4 * q + 3] = f4.w;
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t 
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < CR_ROWS; ++k) {
+            for (int k = 0; k < ROWS; ++k) {
                 const bool in = i0 + k < nrows;
                 fl[k] = in ? row_ovf[t0 + i0 + k] : 0;
                 wk[k] = in ? order[t0 + i0 + k] : 0;
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t 
         uint64_t cls = 0;   // 4 bits per row: its work class
         uint64_t ccnt = 0;  // 8 bits per class: rows of this thread in it
 #pragma unroll
-        for (int k = 0; k < CR_ROWS; ++k) {
+        for (int k = 0; k < ROWS; ++k) {
             if (i0 + k < nrows) {
                 bits |= fl[k] != 0 ? (1u << k) : 0u;
                 const uint32_t c = (uint32_t)work_class(wk[k]);
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t 
         }
         uint64_t used = 0;  // 8 bits per class: rows placed so far
 #pragma unroll
-        for (int k = 0; k < CR_ROWS; ++k) {
+        for (int k = 0; k < ROWS; ++k) {
             if (i0 + k < nrows) {
                 const int c = (int)((cls >> (4 * k)) & 0xFu);
                 int p = 0;
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t 
         }
         __syncthreads();
 #pragma unroll 4
-        for (int k = 0; k < CR_ROWS; ++k) {
+        for (int k = 0; k < ROWS; ++k) {
             const int i = k * CR_THREADS + tid;
             if (i < nrows)
                 order[t0 + i] = sord[i];
@@ -201,10 +205,15 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
                                int32_t *order, hipStream_t s)
 {
     const bool vec = ((reinterpret_cast<uintptr_t>(row_ovf) | reinterpret_cast<uintptr_t>(order)) & 15u) == 0;
-    if (vec)
-        compact_rows_kernel<true><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
+    const bool one_pass8 = T <= CR_THREADS * 8;  // ROWS = 8 only where its single pass is the single chunk
+    if (vec && one_pass8)
+        compact_rows_kernel<true, 8><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
+    else if (vec)
+        compact_rows_kernel<true, 16><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
+    else if (one_pass8)
+        compact_rows_kernel<false, 8><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
     else
-        compact_rows_kernel<false><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
+        compact_rows_kernel<false, 16><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
     return hipGetLastError();
 }
 
