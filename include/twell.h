@@ -13,7 +13,7 @@
  *               twell_ffn_from_gate (the layer after twell_pack_gate[_stats]),
  *               twell_pack_gate, twell_partition_overflow, twell_pack_gate_hybrid,
  *               twell_ffn_fused, twell_ffn_overflow, twell_ffn_hybrid,
- *               twell_ffn_decode (T <= 64)
+ *               twell_ffn_decode (T <= 64), twell_ffn_decode_noalloc
  *   statistics  twell_pack_gate_stats
  *   training    twell_dense_to_hybrid, twell_hybrid_to_dense,
  *               twell_compact_hybrid, twell_compact_to_dense, twell_ffn_backward
@@ -45,9 +45,11 @@
  *     queued: NULL pointer, pointer not 16-byte aligned, bad shape, unsupported
  *     tile width / capacity / dtype, workspace too small.  A failed launch
  *     returns TWELL_E_HIP.  Overflow is data, not an error.
- *   - No C++ exception crosses this interface; the library keeps no mutable
- *     global state.  Concurrent calls on different streams are safe when their
- *     output and workspace buffers do not overlap.
+ *   - No C++ exception crosses this interface.  The library keeps no mutable
+ *     global state, except the static scratch array of
+ *     twell_ffn_decode_noalloc and its per-device address.  Concurrent calls
+ *     on different streams are safe when their output and workspace buffers
+ *     do not overlap (twell_ffn_decode_noalloc: see its own note).
  */
 #ifndef TWELL_H
 #define TWELL_H
@@ -72,7 +74,8 @@ enum twell_status {
     TWELL_E_SHAPE = -3,       /* T < 0, T*n_b too large, d % 64 != 0, F % tile_w != 0, ... */
     TWELL_E_UNSUPPORTED = -4, /* tile_w not in {32,64,128,256}, cap not in [1, tile_w], dtype */
     TWELL_E_HIP = -5,         /* the HIP runtime refused a launch */
-    TWELL_E_WORKSPACE = -6    /* workspace pointer NULL or smaller than required */
+    TWELL_E_WORKSPACE = -6,   /* workspace pointer NULL or smaller than required */
+    TWELL_E_SCRATCH = -7      /* the call needs more than the static scratch array holds */
 };
 
 enum twell_dtype { TWELL_F32 = 0, TWELL_BF16 = 1 };
@@ -294,6 +297,24 @@ TWELL_API size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t 
 TWELL_API int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
                                const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/* twell_ffn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments (minus the workspace),
+ * same checks, same kernels and the same output bits as twell_ffn_decode.
+ * Its scratch is a 16 MiB array in the library's device code: each GPU the
+ * library runs on holds one copy from the first call on it until the process
+ * ends.  The first call on a device looks up that copy's address
+ * (hipGetSymbolAddress) and keeps it; no call allocates or frees anything.
+ * Every call on one GPU uses the same copy and finds there whatever the last
+ * call left; what must start at zero is cleared by the call's own kernels.
+ * Calls that overlap in time on one GPU (e.g. on two streams) race on the
+ * scratch: serialise them.
+ * Limit: twell_ffn_decode_workspace_bytes(T, F, d, tile_w) <= 16 MiB, which
+ * holds every shape twell_ffn_decode accepts with d <= 2048; larger needs
+ * return TWELL_E_SCRATCH before anything is queued. */
+TWELL_API int twell_ffn_decode_noalloc(const void *x, const void *wg_t, const void *wu_t, const void *wd,
+                                       int32_t d, const twell_hybrid_t *hy, float *y, void *stream);
 
 /* Bytes of device workspace twell_ffn_backward needs for these sizes (0 when
  * they are invalid). */

@@ -23,12 +23,12 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 106
+    assert lib.twell_version() == 107
 
 
 def test_status_strings():
     lib = tw.load()
-    for st in range(0, -7, -1):
+    for st in range(0, -8, -1):
         assert lib.twell_status_str(st)
     assert lib.twell_status_str(-99) == b"unknown status"
 
@@ -159,6 +159,32 @@ def test_ffn_decode_validation():
              None) == -4                                                                        # T * F > 2^20
     assert f(GOOD, GOOD, GOOD, GOOD, 60, ctypes.byref(ok), GOOD, GOOD, need, None) == -3        # d % 64
     assert f(None, None, None, None, 64, ctypes.byref(hy(T=0)), None, None, 0, None) == 0       # nothing to do
+
+
+def test_ffn_decode_noalloc_validation():
+    """The same checks as twell_ffn_decode (no workspace argument), and a
+    shape whose workspace exceeds the 16 MiB static scratch is rejected with
+    TWELL_E_SCRATCH before anything touches the GPU."""
+    lib = tw.load()
+    f = lib.twell_ffn_decode_noalloc
+    hy = lambda **k: tw.TwellHybridT(_desc(**k), 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)  # noqa: E731
+    ok = hy()
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, None, GOOD, None) == -1
+    assert f(GOOD, GOOD, None, GOOD, 64, ctypes.byref(ok), GOOD, None) == -1                    # W_u NULL
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(ok), GOOD + 4, None) == -2                # y misaligned
+    assert f(GOOD + 8, GOOD, GOOD, GOOD, 64, ctypes.byref(ok), GOOD, None) == -2                # x misaligned
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(hy(T=65)), GOOD, None) == -4              # T > 64
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(hy(vd=0)), GOOD, None) == -4              # fp32
+    assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(hy(T=64, F=32768, w=256)), GOOD, None) == -4
+    assert f(GOOD, GOOD, GOOD, GOOD, 60, ctypes.byref(ok), GOOD, None) == -3                    # d % 64
+    assert f(None, None, None, None, 64, ctypes.byref(hy(T=0)), None, None) == 0                # nothing to do
+    # d = 4096: (1024 + T) partial rows of 16 KiB exceed the 16 MiB scratch
+    assert lib.twell_ffn_decode_workspace_bytes(1, 512, 4096, 128) > 16 << 20
+    assert f(GOOD, GOOD, GOOD, GOOD, 4096, ctypes.byref(hy(T=1)), GOOD, None) == -7
+    assert b"static" in lib.twell_status_str(-7)
+    # every d <= 2048 shape the decode path accepts fits (largest: T * F = 2^20, d = 2048)
+    assert lib.twell_ffn_decode_workspace_bytes(64, 16384, 2048, 32) <= 16 << 20
+    assert lib.twell_ffn_decode_workspace_bytes(1, 1 << 20, 2048, 256) <= 16 << 20
 
 
 def test_conversion_validation():

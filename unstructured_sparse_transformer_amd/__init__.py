@@ -10,7 +10,7 @@ The functions carry the C names (``include/twell.h``):
 ``twell_pack_gate_hybrid``,
 ``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
 ``twell_ffn_hybrid_workspace_bytes``, ``twell_ffn_decode``,
-``twell_ffn_decode_workspace_bytes``, ``twell_dense_to_hybrid``,
+``twell_ffn_decode_workspace_bytes``, ``twell_ffn_decode_noalloc``, ``twell_dense_to_hybrid``,
 ``twell_hybrid_to_dense``, ``twell_compact_min_bytes``, ``twell_compact_hybrid``,
 ``twell_compact_to_dense``, ``twell_ffn_backward``,
 ``twell_ffn_backward_workspace_bytes``.
@@ -41,10 +41,10 @@ LIB_PATH = os.path.join(_HERE, "libtwell.so")
 
 TWELL_F32, TWELL_BF16 = 0, 1
 STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_SHAPE",
-          -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE"}
+          -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE", -7: "TWELL_E_SCRATCH"}
 EXPORTS = ("twell_ffn_forward", "twell_ffn_from_gate", "twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
            "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
-           "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_dense_to_hybrid", "twell_hybrid_to_dense",
+           "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_ffn_decode_noalloc", "twell_dense_to_hybrid", "twell_hybrid_to_dense",
            "twell_compact_min_bytes", "twell_compact_hybrid", "twell_compact_to_dense",
            "twell_ffn_backward_workspace_bytes", "twell_ffn_backward", "twell_status_str", "twell_version")
 
@@ -95,6 +95,7 @@ def load(path: str = LIB_PATH):
     lib.twell_ffn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.twell_ffn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.twell_ffn_decode.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P, ctypes.c_size_t, P]
+    lib.twell_ffn_decode_noalloc.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P]
     lib.twell_dense_to_hybrid.argtypes = [P, ctypes.POINTER(TwellHybridT), P]
     lib.twell_hybrid_to_dense.argtypes = [ctypes.POINTER(TwellHybridT), P, P]
     lib.twell_compact_min_bytes.argtypes = [I32]
@@ -110,7 +111,7 @@ def load(path: str = LIB_PATH):
     lib.twell_version.restype = ctypes.c_int
     for fn in (lib.twell_pack_gate, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
                lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_forward,
-               lib.twell_ffn_from_gate, lib.twell_ffn_decode,
+               lib.twell_ffn_from_gate, lib.twell_ffn_decode, lib.twell_ffn_decode_noalloc,
                lib.twell_dense_to_hybrid, lib.twell_hybrid_to_dense, lib.twell_compact_hybrid,
                lib.twell_compact_to_dense, lib.twell_ffn_backward):
         fn.restype = ctypes.c_int
@@ -346,6 +347,13 @@ def twell_ffn_decode(x, wg_t, wu_t, wd, hy: Hybrid, y, workspace, stream=None):
     _check("twell_ffn_decode",
            lib.twell_ffn_decode(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), int(x.shape[1]), ctypes.byref(hy.desc()),
                                 _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def twell_ffn_decode_noalloc(x, wg_t, wu_t, wd, hy: Hybrid, y, stream=None):
+    """twell_ffn_decode on the library's static scratch (no workspace argument)."""
+    _check("twell_ffn_decode_noalloc",
+           load().twell_ffn_decode_noalloc(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), int(x.shape[1]),
+                                           ctypes.byref(hy.desc()), _ptr(y), _stream(stream)))
 
 
 def decode_workspace(T: int, F: int, d: int, tile_w: int, device="cuda"):

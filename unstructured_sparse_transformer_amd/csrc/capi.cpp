@@ -1,6 +1,7 @@
 // capi.cpp -- the C ABI declared in include/twell.h: argument checks on the
-// host, then launches on the caller's stream.  Nothing here allocates,
-// synchronises or keeps state between calls.
+// host, then launches on the caller's stream.  Nothing here allocates or
+// synchronises; the only state kept between calls is the per-device address
+// of twell_ffn_decode_noalloc's static scratch (decode.hip).
 #include "twell.h"
 
 #include <hip/hip_runtime.h>
@@ -138,11 +139,46 @@ int launch_from_gate(const void *x, const void *wg_t, const void *wu_t, const vo
                                          splits, s));
 }
 
+// Checks of the decode-shaped calls, apart from their workspace (T == 0
+// passes once the shape is valid).
+int check_decode(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                 const twell_hybrid_t *hy, const float *y)
+{
+    if (!hy)
+        return TWELL_E_NULL;
+    const twell_t *h = &hy->ell;
+    TWELL_TRY(check_layout(h, d));
+    TWELL_TRY(check_hybrid(hy));
+    if (h->vdtype != TWELL_BF16 || h->T > twell::DEC_MAX_T || (int64_t)h->T * h->F > twell::DEC_MAX_TF ||
+        h->F / h->tile_w > twell::DEC_MAX_NB)
+        return TWELL_E_UNSUPPORTED;
+    if (h->T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wg_t));
+    TWELL_TRY(check_mat(wu_t));
+    TWELL_TRY(check_mat(wd));
+    TWELL_TRY(check_mat(y));
+    return check_ptrs(h);
+}
+
+// The decode-shaped layer on a carved workspace, arguments already checked.
+int launch_decode(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                  const twell_hybrid_t *hy, float *y, const twell::DecodeWs &w, hipStream_t s)
+{
+    const twell_t *h = &hy->ell;
+    TWELL_TRY(hip_status(twell::launch_decode_gate_pack(x, wg_t, h->T, d, h->F, h->tile_w, h->cap, h->val, h->idx,
+                                                        h->cnt, hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->order,
+                                                        hy->max_ovf, w, s)));
+    return hip_status(twell::launch_ffn_decode(h->cnt, h->val, h->idx, h->T, h->F, h->tile_w, h->cap, x, wu_t, wd, d,
+                                               hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->max_ovf, hy->dense, y, w, s));
+}
+
 }  // namespace
 
 extern "C" {
 
-int twell_version(void) { return 106; }
+int twell_version(void) { return 107; }
 
 const char *twell_status_str(int status)
 {
@@ -161,6 +197,8 @@ const char *twell_status_str(int status)
         return "HIP launch failed";
     case TWELL_E_WORKSPACE:
         return "workspace missing or too small";
+    case TWELL_E_SCRATCH:
+        return "the call needs more scratch than the library's static array holds (16 MiB per GPU)";
     default:
         return "unknown status";
     }
@@ -387,35 +425,33 @@ size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t
 int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
                      const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (!hy)
-        return TWELL_E_NULL;
-    const twell_t *h = &hy->ell;
-    TWELL_TRY(check_layout(h, d));
-    TWELL_TRY(check_hybrid(hy));
-    if (h->vdtype != TWELL_BF16 || h->T > twell::DEC_MAX_T || (int64_t)h->T * h->F > twell::DEC_MAX_TF ||
-        h->F / h->tile_w > twell::DEC_MAX_NB)
-        return TWELL_E_UNSUPPORTED;
-    if (h->T == 0)
+    TWELL_TRY(check_decode(x, wg_t, wu_t, wd, d, hy, y));
+    if (hy->ell.T == 0)
         return TWELL_OK;
-    TWELL_TRY(check_mat(x));
-    TWELL_TRY(check_mat(wg_t));
-    TWELL_TRY(check_mat(wu_t));
-    TWELL_TRY(check_mat(wd));
-    TWELL_TRY(check_mat(y));
-    TWELL_TRY(check_ptrs(h));
     if (!workspace)
         return TWELL_E_NULL;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return TWELL_E_ALIGN;
+    const twell_t *h = &hy->ell;
     const twell::DecodeWs w = twell::decode_ws_layout(workspace, h->T, h->F, h->tile_w, d);
     if (workspace_bytes < w.bytes)
         return TWELL_E_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    TWELL_TRY(hip_status(twell::launch_decode_gate_pack(x, wg_t, h->T, d, h->F, h->tile_w, h->cap, h->val, h->idx,
-                                                        h->cnt, hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->order,
-                                                        hy->max_ovf, w, s)));
-    return hip_status(twell::launch_ffn_decode(h->cnt, h->val, h->idx, h->T, h->F, h->tile_w, h->cap, x, wu_t, wd, d,
-                                               hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->max_ovf, hy->dense, y, w, s));
+    return launch_decode(x, wg_t, wu_t, wd, d, hy, y, w, static_cast<hipStream_t>(stream));
+}
+
+int twell_ffn_decode_noalloc(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
+                             const twell_hybrid_t *hy, float *y, void *stream)
+{
+    TWELL_TRY(check_decode(x, wg_t, wu_t, wd, d, hy, y));
+    if (hy->ell.T == 0)
+        return TWELL_OK;
+    const twell_t *h = &hy->ell;
+    if (twell::decode_ws_layout(nullptr, h->T, h->F, h->tile_w, d).bytes > twell::DEC_STATIC_BYTES)
+        return TWELL_E_SCRATCH;
+    void *scratch = nullptr;
+    TWELL_TRY(hip_status(twell::decode_static_workspace(&scratch)));
+    const twell::DecodeWs w = twell::decode_ws_layout(scratch, h->T, h->F, h->tile_w, d);
+    return launch_decode(x, wg_t, wu_t, wd, d, hy, y, w, static_cast<hipStream_t>(stream));
 }
 
 int twell_ffn_fused(const twell_t *h, const int32_t *order, const void *x, const void *wu_t, const void *wd,

@@ -33,4 +33,13 @@ struct DecodeWs {
 // nullptr only `bytes` is meaningful.
 DecodeWs decode_ws_layout(void *base, int T, int F, int tile_w, int d);
 
+// Size of the static scratch array behind twell_ffn_decode_noalloc.  Every
+// decode shape with d <= 2048 fits: z is at most 2^20 floats (4 MiB) and the
+// partial rows (DEC_BASE_CHUNKS + T) x d floats (8.5 MiB at d = 2048).
+constexpr size_t DEC_STATIC_BYTES = (size_t)16 << 20;
+
+// Device address of the static scratch's copy on the current device, looked
+// up once per device (no allocation) and kept for later calls.
+hipError_t decode_static_workspace(void **ptr);
+
 }  // namespace twell

@@ -10,12 +10,49 @@
 // it into TwELL, one workgroup per row, and its last workgroup derives the
 // per-row results (overflow flags and list, work order, tile prefixes and the
 // chunking of the rows' entries for the gather in ffn_fused.hip).
+#include <mutex>
+
 #include "decode.h"
 #include "launch.h"
 #include "twell_device.h"
 #include "wave_ops.h"
 
+// Workspace of twell_ffn_decode_noalloc, for callers that cannot allocate
+// (graph capture, serving loops).  A device array of the code object: every
+// GPU the library runs on holds its own copy, at its own address, until the
+// process ends.  On the host the array's name is only a stand-in, never a
+// device address: host code uses the address hipGetSymbolAddress returns for
+// the current device (decode_static_workspace), kept per device.  Calls on
+// one GPU share the copy, so calls that overlap in time on one GPU race.
+static __device__ __align__(256) char scratch[twell::DEC_STATIC_BYTES];
+
 namespace twell {
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[SCRATCH_MAX_DEVICES];
+}  // namespace
+
+hipError_t decode_static_workspace(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return hipSuccess;
+}
 
 // ------------------------------------------------------------------ gate
 // z[m][n0 + n] for the workgroup's 32 neurons n, all rows m < T (MB blocks of
