@@ -23,6 +23,8 @@ Models", gist.science summary page):
   per-neuron active counts and per (row, tile) sums of the active gate values.
 * ``ffn_backward``: the gradients of the FFN (section 2.4's training
   kernels), per active (row, neuron) in ascending order.
+* ``abs_sums`` / ``gamma``: not results of the method but the magnitudes
+  that bound summation-order rounding (the gate's tie band, y's tolerance).
 * ``compact_hybrid`` / ``compact_to_dense``: section 2.3's compact storage of
   the hybrid (reading: exact entries per fitting row, dense overflow rows).
 * ``hybrid_to_dense``: section 2.4's hybrid-to-dense conversion; the
@@ -39,7 +41,9 @@ one live neuron), for ``hybrid_to_dense`` the exact round trip through the
 dense-to-hybrid direction and a hand-built example, and for ``compact_hybrid``
 the hand example, the exact round trip and nonzero conservation, and for
 ``ffn_backward`` central finite differences of an independent numpy forward,
-the matrix form with numpy matmuls, and a one-neuron closed form.
+the matrix form with numpy matmuls, and a one-neuron closed form; for
+``abs_sums`` pure-Python brute force and the closed form for non-negative
+inputs (equal to the dot product itself).
 """
 
 from __future__ import annotations
@@ -104,6 +108,23 @@ def gate(x: np.ndarray, wg_t: np.ndarray) -> np.ndarray:
 def up(x: np.ndarray, wu_t: np.ndarray) -> np.ndarray:
     """u = x . W_u in fp64 (numpy matmul)."""
     return _c(x, np.float64) @ _c(wu_t, np.float64).T
+
+
+def abs_sums(x: np.ndarray, w_t: np.ndarray) -> np.ndarray:
+    """M[t][j] = sum_k |x[t][k] * w_t[j][k]| in fp64 (numpy matmul of the
+    absolute values).  Not a result of the method: it is the magnitude that
+    bounds the rounding error of the dot product x[t] . w_t[j] in any
+    summation order, |fl(x.w) - x.w| <= gamma(d) * M, gamma(n) = n u / (1 - n u)
+    for unit roundoff u.  With W_g it is the tie band of the gate: an entry
+    with |z| <= gamma(d) M may be active in one summation order and not in
+    another."""
+    return np.abs(_c(x, np.float64)) @ np.abs(_c(w_t, np.float64)).T
+
+
+def gamma(n: int, unit: float = 2.0 ** -23) -> float:
+    """n u / (1 - n u): the relative error bound of an n-term sum in floating
+    point of unit roundoff u (default 2^-23, fp32 with any rounding mode)."""
+    return n * unit / (1.0 - n * unit)
 
 
 def matmul_rows(a: np.ndarray, rows, b_t: np.ndarray) -> np.ndarray:
@@ -325,8 +346,9 @@ class Reference:
     y_fused: np.ndarray    # [R][d] fused-only y: overflow rows 0, stored h
 
 
-def reference(wl, rows=None, use_blas: bool = True) -> Reference:
-    """Everything the path computes for `wl` (a workloads.Workload) on `rows`."""
+def reference(wl, rows=None, use_blas: bool = True, with_y: bool = True) -> Reference:
+    """Everything the path computes for `wl` (a workloads.Workload) on `rows`
+    (with_y=False: the gate, TwELL and partition only; the y fields are None)."""
     if rows is None:
         rows = np.arange(wl.T)
     rows = np.asarray(rows, np.int64)
@@ -334,6 +356,8 @@ def reference(wl, rows=None, use_blas: bool = True) -> Reference:
     z = gate(x, wl.wg_t) if use_blas else matmul_rows(x, np.arange(len(rows)), wl.wg_t)
     tw = pack_twell(z, wl.tile_w, wl.cap, wl.dtype)
     row_ovf, ovf_local, _ = partition_overflow(tw.cnt, wl.cap)
+    if not with_y:
+        return Reference(rows, z, tw, row_ovf, ovf_local, None, None, None)
     y_exact = ffn_active(z, x, wl.wu_t, wl.wd, None)
     y_stored = ffn_active(z, x, wl.wu_t, wl.wd, wl.dtype)
     y_fused = ffn_twell(tw, x, wl.wu_t, wl.wd, skip_overflow=True)

@@ -236,3 +236,29 @@ def test_binding_requires_library(tmp_path, monkeypatch):
     monkeypatch.setattr(tw, "_lib", None)
     with pytest.raises(RuntimeError, match="libtwell.so not found"):
         tw.load(str(tmp_path / "missing.so"))
+
+
+def test_ffn_backward_validation():
+    """Host checks of twell_ffn_backward, including the bound on the entry
+    scan's int32 count: T * n_b * cap + max_ovf * F must stay below 2^31."""
+    lib = tw.load()
+    f = lib.twell_ffn_backward
+
+    def hy(max_ovf=8, **k):
+        return tw.TwellHybridT(_desc(**k), max_ovf, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
+
+    def call(h, d=64, max_entries=16, ws=GOOD, ws_bytes=1 << 30):
+        return f(ctypes.byref(h) if h is not None else None, GOOD, GOOD, GOOD, GOOD, d, GOOD, GOOD, GOOD, GOOD,
+                 GOOD, max_entries, ws, ws_bytes, None)
+
+    assert call(None) == -1
+    assert call(hy(vd=0)) == -4                      # fp32
+    assert call(hy(), d=4096) == -4                  # d > 2048
+    assert call(hy(), max_entries=-1) == -3
+    assert call(hy(), ws=None) == -1
+    assert call(hy(), ws=GOOD + 16) == -2
+    assert call(hy(), ws_bytes=0) == -6
+    # 7 * 2^28 fitting-row slots (< 2^31 on their own) + 2^14 dense rows of 2^14 = 2^31 entries
+    big = dict(T=1 << 19, F=16384, w=32, cap=7)
+    assert call(hy(max_ovf=1 << 14, **big), d=2048, ws_bytes=0) == -3
+    assert call(hy(max_ovf=(1 << 14) - 1, **big), d=2048, ws_bytes=0) == -6   # one row less: next check

@@ -449,3 +449,54 @@ def test_backward_single_neuron_closed_form():
     want_dx = np.where(act[:, None], g[:, None] * (h[:, None] * wl.wu_t[j].astype(np.float64)
                                                     + u[:, None] * wl.wg_t[j].astype(np.float64)), 0.0)
     np.testing.assert_allclose(dx, want_dx, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ magnitude sums (tie band, y tolerance)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_abs_sums_against_brute_force(seed):
+    """sum_k |x_k w_jk| with mixed signs, against pure-Python loops."""
+    rng = np.random.default_rng(100 + seed)
+    x = rng.standard_normal((3, 7)).astype(np.float32)
+    w = rng.standard_normal((5, 7)).astype(np.float32)
+    m = oracle.abs_sums(x, w)
+    for t in range(3):
+        for j in range(5):
+            s = 0.0
+            for k in range(7):
+                s += abs(float(x[t, k]) * float(w[j, k]))
+            assert m[t, j] == pytest.approx(s, rel=1e-15, abs=0.0)
+
+
+def test_abs_sums_closed_forms():
+    """Non-negative operands: the magnitude sum is the dot product itself;
+    gamma(2048) at fp32's unit 2^-23 is 2^-12 / (1 - 2^-12) = 1/4095."""
+    rng = np.random.default_rng(7)
+    x = np.abs(rng.standard_normal((4, 16))).astype(np.float32)
+    w = np.abs(rng.standard_normal((6, 16))).astype(np.float32)
+    np.testing.assert_allclose(oracle.abs_sums(x, w), oracle.gate(x, w), rtol=1e-15)
+    assert oracle.gamma(2048) == pytest.approx(1.0 / 4095.0, rel=1e-15)
+    assert oracle.gamma(1, 2.0 ** -24) == pytest.approx(2.0 ** -24 / (1 - 2.0 ** -24), rel=1e-15)
+
+
+def test_tie_band_bounds_fp32_orders():
+    """Continuous bf16-valued inputs: fp32 sums of x.w in several orders all
+    lie within gamma(d) * sum|x w| of the fp64 value (the tie band is a valid
+    bound on summation-order effects)."""
+    import torch
+    rng = np.random.default_rng(9)
+    d = 512
+    x = torch.from_numpy(rng.standard_normal((8, d)).astype(np.float32)).bfloat16().float().numpy()
+    w = torch.from_numpy((rng.standard_normal((64, d)) / np.sqrt(d)).astype(np.float32)).bfloat16().float().numpy()
+    z = oracle.gate(x, w)
+    band = oracle.gamma(d) * oracle.abs_sums(x, w)
+    prods = x[:, None, :] * w[None, :, :]            # exact in fp32 (bf16 x bf16)
+    fwd = np.zeros((8, 64), np.float32)
+    for k in range(d):
+        fwd = fwd + prods[:, :, k]
+    rev = np.zeros((8, 64), np.float32)
+    for k in reversed(range(d)):
+        rev = rev + prods[:, :, k]
+    pair = prods.sum(axis=2, dtype=np.float32)
+    for s in (fwd, rev, pair):
+        assert (np.abs(s.astype(np.float64) - z) <= band).all()
+    assert (fwd != rev).any()  # the orders do differ: the check is not vacuous

@@ -4,43 +4,16 @@ import numpy as np
 import pytest
 
 import oracle
+from helpers import grid_ok
 from workloads import (bf16_representable, make_decode_windows, make_layer_0p5b, make_layer_2b,
                        make_random_small, make_stress_layer, make_tiny)
 from workloads.gen import stress_layer_mean
 
 
-def _grid_ok(wl):
-    """Every partial sum of x_t . w_j stays below 2^7 and every product is a multiple of 2^-17.
-
-    Bound: |sum_k<d-1 x_k w_k| <= ||x_t[:-1]|| ||w_j[:-1]|| (Cauchy-Schwarz), plus |x_t,last * w_j,last|.
-    """
-    x = wl.x.astype(np.float64)
-    for w in (wl.wg_t, wl.wu_t):
-        w = w.astype(np.float64)
-        fin = np.isfinite(w[:, -1])
-        nx = np.sqrt((x[:, :-1] ** 2).sum(1)).max()
-        nw = np.sqrt((w[:, :-1] ** 2).sum(1)).max()
-        bias = np.abs(x[:, -1]).max() * np.abs(w[fin, -1]).max()
-        assert nx * nw + bias < 128.0, (wl.name, nx, nw, bias)
-    # grids: x body on 2^-4, weights on 2^-10, last column of x >= 2^-3 and bf16,
-    # finite biases bf16 (or 2^-10 grid for fp32) with magnitude >= 1
-    assert np.all(np.rint(wl.x[:, :-1] * 16) == wl.x[:, :-1] * 16)
-    for w in (wl.wg_t[:, :-1], wl.wu_t, wl.wd):
-        assert np.all(np.rint(w * 1024) == w * 1024)
-    assert np.all(wl.x[:, -1] >= 0.125)
-    fb = wl.wg_t[np.isfinite(wl.wg_t[:, -1]), -1]
-    assert np.all(np.abs(fb) >= 1.0)
-    if wl.dtype == "bf16":
-        assert bf16_representable(wl.x) and bf16_representable(wl.wu_t) and bf16_representable(wl.wd)
-        assert bf16_representable(wl.wg_t[np.isfinite(wl.wg_t)])
-    else:
-        assert np.all(np.rint(fb * 1024) == fb * 1024)
-
-
 def test_tiny_grid_and_rate():
     wl = make_tiny()
     assert (wl.T, wl.d, wl.F, wl.dtype, wl.tile_w, wl.cap) == (64, 256, 1024, "f32", 128, 16)
-    _grid_ok(wl)
+    grid_ok(wl)
     z = oracle.gate(wl.x, wl.wg_t)
     p = (z > 0).mean()
     n = z.size
@@ -51,7 +24,7 @@ def test_tiny_grid_and_rate():
 def test_0p5b_grid_and_rate():
     wl = make_layer_0p5b()
     assert (wl.T, wl.d, wl.F, wl.dtype, wl.tile_w, wl.cap) == (4096, 1024, 4096, "bf16", 128, 8)
-    _grid_ok(wl)
+    grid_ok(wl)
     z = oracle.gate(wl.x[:512], wl.wg_t)
     p = (z > 0).mean()
     assert abs(p - 0.01) < 0.0015
@@ -62,7 +35,7 @@ def test_0p5b_grid_and_rate():
 def test_2b_grid_dead_and_mean():
     wl = make_layer_2b()
     assert (wl.T, wl.d, wl.F, wl.dtype, wl.tile_w, wl.cap) == (8192, 2048, 8192, "bf16", 256, 16)
-    _grid_ok(wl)
+    grid_ok(wl)
     dead = wl.meta["dead"]
     assert len(dead) == 1638 and np.isneginf(wl.wg_t[dead, -1]).all()
     assert np.isfinite(wl.wg_t[:, -1]).sum() == 8192 - 1638
@@ -86,7 +59,7 @@ def test_decode_windows():
 @pytest.mark.parametrize("layer", [0, 23])
 def test_stress_layer(layer):
     wl = make_stress_layer(layer, T=2048)
-    _grid_ok(wl)
+    grid_ok(wl)
     z = oracle.gate(wl.x, wl.wg_t)
     n = (z > 0).sum(1)
     stress = wl.meta["stress_rows"]
@@ -104,7 +77,7 @@ def test_stress_layer_means_profile():
 
 def test_random_small_grid():
     for s in range(3):
-        _grid_ok(make_random_small(100, 64, 256, 64, 4, active_frac=0.1, seed=s, jitter=0.5))
+        grid_ok(make_random_small(100, 64, 256, 64, 4, active_frac=0.1, seed=s, jitter=0.5))
 
 
 def test_seed_streams_independent_of_shape():
@@ -112,3 +85,22 @@ def test_seed_streams_independent_of_shape():
     b = make_stress_layer(3, T=128)
     np.testing.assert_array_equal(a.wg_t[:, :-1], b.wg_t[:, :-1])
     np.testing.assert_array_equal(a.wd, b.wd)
+
+
+def test_continuous_mode():
+    """Continuous mode: same shapes and bias structure, values representable
+    in the storage type but off the grid; grid mode is unchanged by it."""
+    from workloads import make_random_small
+    g = make_random_small(64, 128, 512, 128, 8, "bf16", active_frac=0.05, seed=5, jitter=0.5)
+    c = make_random_small(64, 128, 512, 128, 8, "bf16", active_frac=0.05, seed=5, jitter=0.5, mode="continuous")
+    assert c.x.shape == g.x.shape and c.wg_t.shape == g.wg_t.shape
+    assert bf16_representable(c.x) and bf16_representable(c.wg_t) and bf16_representable(c.wd)
+    off = c.x[:, :-1] * 16 - np.rint(c.x[:, :-1] * 16)
+    assert np.abs(off).max() > 0.1                       # not on the 2^-4 grid
+    np.testing.assert_array_equal(c.x[:, -1], g.x[:, -1])  # same jitter column
+    np.testing.assert_array_equal(c.wg_t[:, -1], g.wg_t[:, -1])  # same biases
+    assert abs(c.wg_t[:, :-1].std() * np.sqrt(128) - 1) < 0.05
+    f = make_random_small(32, 64, 256, 64, 4, "f32", seed=6, mode="continuous")
+    assert not bf16_representable(f.x)                    # fp32 layers keep full fp32 values
+    g2 = make_random_small(64, 128, 512, 128, 8, "bf16", active_frac=0.05, seed=5, jitter=0.5)
+    np.testing.assert_array_equal(g.x, g2.x)

@@ -364,6 +364,11 @@ int twell_ffn_backward(const twell_hybrid_t *hy, const void *x, const void *wg_t
         return TWELL_E_UNSUPPORTED;
     if (max_entries < 0)
         return TWELL_E_SHAPE;
+    // The entry scan counts in int32: the stored entries of the rows that fit
+    // (at most T * n_b * cap) plus the nonzeros of the held dense rows (at
+    // most max_ovf * F) must stay below 2^31.
+    if ((int64_t)e->T * (e->F / e->tile_w) * e->cap + (int64_t)hy->max_ovf * e->F >= ((int64_t)1 << 31))
+        return TWELL_E_SHAPE;
     TWELL_TRY(check_mat(wg_t));
     TWELL_TRY(check_mat(wu_t));
     TWELL_TRY(check_mat(wd));

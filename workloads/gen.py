@@ -1,4 +1,5 @@
-"""Deterministic synthetic workloads on an exact-accumulation grid.
+"""Deterministic synthetic workloads, on an exact-accumulation grid (the
+default, "grid" mode) or off it ("continuous" mode).
 
 Every array is drawn from its own PCG64 stream,
 ``SeedSequence(0, spawn_key=(workload_id, layer, array_id))``, so changing one
@@ -18,6 +19,13 @@ Grid construction (what makes GPU and CPU agree bit for bit on z = x.W_g):
   partial sum stays below 2^7 in magnitude, fp32 accumulation in ANY order is
   exact.  The tests check that bound for every workload (Cauchy-Schwarz on the
   non-bias part plus the bias term).
+
+Continuous mode (``mode="continuous"``; the 0.5B and 2B layers, decode
+windows and random small layers): x ~ N(0,1) and weights ~ N(0, 1/d) rounded
+to the storage type (bf16, or plain fp32 values for fp32 layers), with the same
+last-column / bias structure.  There fp32 sums depend on their order, so a gate
+value near 0 may be active on one side only; tests compare such inputs within
+the tie band instead of bit for bit.
 
 All arrays are float32 holding values that are exactly representable in the
 workload's dtype ("bf16" or "f32"); -inf appears only in W_g^T's last column.
@@ -89,6 +97,31 @@ def bf16_representable(a) -> bool:
     return bool(np.all((a.view(np.uint32) & 0xFFFF) == 0))
 
 
+def _cont_x(rng, shape, dtype: str) -> np.ndarray:
+    """Continuous mode: N(0,1) rounded to the storage type (no grid)."""
+    a = rng.standard_normal(shape, dtype=np.float32)
+    return round_to_bf16(a) if dtype == "bf16" else a
+
+
+def _cont_w(rng, shape, d, dtype: str) -> np.ndarray:
+    a = ((1.0 / np.sqrt(d)) * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+    return round_to_bf16(a) if dtype == "bf16" else a
+
+
+def _draw_x(rng, shape, mode: str, dtype: str) -> np.ndarray:
+    if mode == "grid":
+        return _grid_x(rng, shape)
+    assert mode == "continuous", mode
+    return _cont_x(rng, shape, dtype)
+
+
+def _draw_w(rng, shape, d, mode: str, dtype: str) -> np.ndarray:
+    if mode == "grid":
+        return _grid_w(rng, shape, d)
+    assert mode == "continuous", mode
+    return _cont_w(rng, shape, d, dtype)
+
+
 def _grid_x(rng, shape) -> np.ndarray:
     g = np.rint(16.0 * rng.standard_normal(shape, dtype=np.float32))
     np.clip(g, -127, 127, out=g)
@@ -128,18 +161,18 @@ def make_tiny() -> Workload:
                     {"target_active_frac": 0.03, "tau": tau, "bias": float(wg[0, d - 1])})
 
 
-def make_layer_0p5b() -> Workload:
+def make_layer_0p5b(mode: str = "grid") -> Workload:
     """4096 tokens, d=1024, F=4096, bf16, ~1% active, tile 128, capacity 8."""
     T, d, F = 4096, 1024, 4096
-    x = _grid_x(_rng(WID_0P5B, 0, AID_X), (T, d))
+    x = _draw_x(_rng(WID_0P5B, 0, AID_X), (T, d), mode, "bf16")
     x[:, d - 1] = 1.0
-    wg = _grid_w(_rng(WID_0P5B, 0, AID_WG), (F, d), d)
-    wu = _grid_w(_rng(WID_0P5B, 0, AID_WU), (F, d), d)
-    wd = _grid_w(_rng(WID_0P5B, 0, AID_WD), (F, d), d)
+    wg = _draw_w(_rng(WID_0P5B, 0, AID_WG), (F, d), d, mode, "bf16")
+    wu = _draw_w(_rng(WID_0P5B, 0, AID_WU), (F, d), d, mode, "bf16")
+    wd = _draw_w(_rng(WID_0P5B, 0, AID_WD), (F, d), d, mode, "bf16")
     tau = _threshold_for_rate(0.01, d)
     wg[:, d - 1] = _bias_bf16(tau)
-    return Workload("layer_0p5b", T, d, F, "bf16", 128, 8, x, wg, wu, wd,
-                    {"target_active_frac": 0.01, "tau": tau, "bias": float(wg[0, d - 1])})
+    return Workload("layer_0p5b" + _suffix(mode), T, d, F, "bf16", 128, 8, x, wg, wu, wd,
+                    {"target_active_frac": 0.01, "tau": tau, "bias": float(wg[0, d - 1]), "mode": mode})
 
 
 def _solve_tau_lognormal_jitter(target_mean: float, live: int, d: int, sigma_j: float) -> float:
@@ -170,43 +203,48 @@ def _solve_tau_lognormal_jitter(target_mean: float, live: int, d: int, sigma_j: 
 _CACHE: dict = {}
 
 
-def make_layer_2b(cache: bool = True) -> Workload:
+def _suffix(mode: str) -> str:
+    return "" if mode == "grid" else "_" + mode
+
+
+def make_layer_2b(cache: bool = True, mode: str = "grid") -> Workload:
     """8192 tokens, d=2048, F=8192, bf16, mean ~29 active, lognormal jitter, 20% dead.
 
     Per-token threshold tau0 * exp(0.5 eps_t): the last column of x holds
     bf16(exp(0.5 eps_t)) and the last column of W_g^T holds bf16(-tau0), or -inf
     for the round(0.2 F) dead neurons.  Tile 256, capacity 16.
     """
-    if cache and "2b" in _CACHE:
-        return _CACHE["2b"]
+    key = "2b" + _suffix(mode)
+    if cache and key in _CACHE:
+        return _CACHE[key]
     T, d, F = 8192, 2048, 8192
-    x = _grid_x(_rng(WID_2B, 0, AID_X), (T, d))
+    x = _draw_x(_rng(WID_2B, 0, AID_X), (T, d), mode, "bf16")
     eps = np.clip(_rng(WID_2B, 0, AID_JITTER).standard_normal(T), -4.0, 4.0)
     x[:, d - 1] = round_to_bf16(np.exp(0.5 * eps).astype(np.float32))
-    wg = _grid_w(_rng(WID_2B, 0, AID_WG), (F, d), d)
-    wu = _grid_w(_rng(WID_2B, 0, AID_WU), (F, d), d)
-    wd = _grid_w(_rng(WID_2B, 0, AID_WD), (F, d), d)
+    wg = _draw_w(_rng(WID_2B, 0, AID_WG), (F, d), d, mode, "bf16")
+    wu = _draw_w(_rng(WID_2B, 0, AID_WU), (F, d), d, mode, "bf16")
+    wd = _draw_w(_rng(WID_2B, 0, AID_WD), (F, d), d, mode, "bf16")
     n_dead = int(round(0.2 * F))
     dead = np.sort(_rng(WID_2B, 0, AID_DEAD).choice(F, n_dead, replace=False))
     tau0 = _solve_tau_lognormal_jitter(29.0, F - n_dead, d, 0.5)
     wg[:, d - 1] = _bias_bf16(tau0)
     wg[dead, d - 1] = -np.inf
-    w = Workload("layer_2b", T, d, F, "bf16", 256, 16, x, wg, wu, wd,
+    w = Workload("layer_2b" + _suffix(mode), T, d, F, "bf16", 256, 16, x, wg, wu, wd,
                  {"target_mean_active": 29.0, "tau0": tau0, "bias": float(_bias_bf16(tau0)),
-                  "dead": dead, "jitter_sigma": 0.5})
+                  "dead": dead, "jitter_sigma": 0.5, "mode": mode})
     if cache:
-        _CACHE["2b"] = w
+        _CACHE[key] = w
     return w
 
 
-def make_decode_windows(T: int, max_windows: int = 512):
+def make_decode_windows(T: int, max_windows: int = 512, mode: str = "grid"):
     """Disjoint consecutive windows of T tokens of the 2B-like layer (same weights)."""
-    base = make_layer_2b()
+    base = make_layer_2b(mode=mode)
     n = min(base.T // T, max_windows)
     out = []
     for i in range(n):
         w = base.rows(i * T, (i + 1) * T)
-        w.name = f"decode_2b_T{T}[{i}]"
+        w.name = f"decode_2b{_suffix(mode)}_T{T}[{i}]"
         out.append(w)
     return out
 
@@ -253,13 +291,13 @@ def make_stress_layer(layer: int, T: int = 16384) -> Workload:
 
 def make_random_small(T: int, d: int, F: int, tile_w: int, cap: int, dtype: str = "bf16",
                       active_frac: float = 0.05, seed: int = 0, jitter: float = 0.0,
-                      n_dead: int = 0) -> Workload:
-    """A grid-mode layer of any shape (tests): ones/jitter column + bias for `active_frac`."""
+                      n_dead: int = 0, mode: str = "grid") -> Workload:
+    """A layer of any shape (tests): ones/jitter column + bias for `active_frac`."""
     assert d >= 2
-    x = _grid_x(_rng(WID_RANDOM, seed, AID_X), (T, d))
-    wg = _grid_w(_rng(WID_RANDOM, seed, AID_WG), (F, d), max(d, 16))
-    wu = _grid_w(_rng(WID_RANDOM, seed, AID_WU), (F, d), max(d, 16))
-    wd = _grid_w(_rng(WID_RANDOM, seed, AID_WD), (F, d), max(d, 16))
+    x = _draw_x(_rng(WID_RANDOM, seed, AID_X), (T, d), mode, dtype)
+    wg = _draw_w(_rng(WID_RANDOM, seed, AID_WG), (F, d), max(d, 16), mode, dtype)
+    wu = _draw_w(_rng(WID_RANDOM, seed, AID_WU), (F, d), max(d, 16), mode, dtype)
+    wd = _draw_w(_rng(WID_RANDOM, seed, AID_WD), (F, d), max(d, 16), mode, dtype)
     sig = np.sqrt((d - 1) / max(d, 16))
     tau = max(_ND.inv_cdf(1.0 - active_frac) * sig, 1.0)
     if jitter > 0:
@@ -271,8 +309,8 @@ def make_random_small(T: int, d: int, F: int, tile_w: int, cap: int, dtype: str 
     if n_dead:
         dead = _rng(WID_RANDOM, seed, AID_DEAD).choice(F, n_dead, replace=False)
         wg[dead, d - 1] = -np.inf
-    return Workload(f"random_T{T}_d{d}_F{F}_w{tile_w}_c{cap}_s{seed}", T, d, F, dtype, tile_w, cap,
-                    x, wg, wu, wd, {"tau": tau})
+    return Workload(f"random_T{T}_d{d}_F{F}_w{tile_w}_c{cap}_s{seed}{_suffix(mode)}", T, d, F, dtype, tile_w,
+                    cap, x, wg, wu, wd, {"tau": tau, "mode": mode})
 
 
 WORKLOADS = {
