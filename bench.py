@@ -192,7 +192,7 @@ def main():
     x, wg, wu, wd = to(wl.x), to(wl.wg_t), to(wl.wu_t), to(wl.wd)
     max_ovf = min(args.max_ovf, wl.T)
     hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
-    ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt)
+    ws = tw.hybrid_workspace(hy, wl.d)
     y = torch.empty((wl.T, wl.d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -229,7 +229,7 @@ def main():
         ev[1].record()
         tw.twell_partition_overflow(x, wg, hy)
         ev[2].record()
-        tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=hy.order)
+        tw.twell_ffn_fused(hy.ell, x, wu, wd, y, ws, order=hy.order)
         ev[3].record()
         tw.twell_ffn_overflow(hy, x, wu, wd, y, ws)
         ev[4].record()
@@ -625,7 +625,7 @@ def run_decode(args, wl, tw, torch, np):
               wl.T * n_b * (4 + wl.cap * (esz + 1)))
     # the batch path on the same rows
     hb = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, torch.bfloat16, wl.T)
-    wsb = tw.hybrid_workspace(wl.T, wl.F, wl.d, torch.bfloat16)
+    wsb = tw.hybrid_workspace(hb, wl.d)
 
     def batch():
         tw.twell_ffn_forward(xv[cur[0] % nw], wg, wu, wd, hb, y, wsb)
@@ -697,7 +697,7 @@ def run_stack(args, tw, torch, np):
         x, wg, wu, wd = to(wl.x), to(wl.wg_t), to(wl.wu_t), to(wl.wd)
         max_ovf = min(args.max_ovf * 4, wl.T)
         hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, torch.bfloat16, max_ovf)
-        ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, torch.bfloat16)
+        ws = tw.hybrid_workspace(hy, wl.d)
         y = torch.empty((wl.T, wl.d), dtype=torch.float32, device=dev)
 
         def step(ev=None):

@@ -164,22 +164,33 @@ TWELL_API int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d,
  *           twell_partition_overflow): rows are started in that order, so the
  *           heavy ones do not trail at the end; NULL = ascending rows.  Each
  *           row's result is the same bits for any order; a non-permutation
- *           leaves some rows unwritten (entries are range-checked). */
+ *           leaves some rows unwritten (entries are range-checked).
+ *   workspace : device, >= twell_workspace_bytes(T, F, tile_w, cap, 0, d,
+ *           vdtype) (it holds each stored entry's partial dot products
+ *           x[t] . W_u^T[j] over 8 column slices of d, from the up pass to
+ *           the down pass), 256-byte aligned, content ignored on entry. */
 TWELL_API int twell_ffn_fused(const twell_t *h, const int32_t *order, const void *x, const void *wu_t,
-                    const void *wd, int32_t d, float *y, void *stream);
+                              const void *wd, int32_t d, float *y, void *workspace, size_t workspace_bytes,
+                              void *stream);
 
-/* Bytes of device workspace twell_ffn_hybrid, twell_ffn_overflow,
- * twell_ffn_forward and twell_ffn_from_gate need for these sizes (0 when
- * max_ovf is 0). */
-TWELL_API size_t twell_ffn_hybrid_workspace_bytes(int32_t max_ovf, int32_t F, int32_t d, int32_t vdtype);
+/* Bytes of device workspace that twell_ffn_fused (with max_ovf = 0),
+ * twell_ffn_overflow, twell_ffn_hybrid, twell_ffn_forward and
+ * twell_ffn_from_gate need for these sizes: T * (F / tile_w) * cap * nch
+ * floats for the fused step's partial dot products (nch = 8 column slices
+ * of d when d is a multiple of 512 (bf16) or 256 (fp32); d / 64 when d is
+ * smaller; more for other widths), plus, when max_ovf > 0, the overflow
+ * rows' gated products and split-K partial sums.  One workspace of
+ * this size serves every one of these calls.  Returns 0 for invalid sizes. */
+TWELL_API size_t twell_workspace_bytes(int32_t T, int32_t F, int32_t tile_w, int32_t cap, int32_t max_ovf,
+                                       int32_t d, int32_t vdtype);
 
 /* Dense part of the hybrid FFN (section 2.3 of the page): for the first
  * min(n_ovf, max_ovf) overflow rows r = ovf_rows[i], writes
  * y[r] = (dense[i] * (x[r] . W_u)) . W_d, the gated product rounded to
  * vdtype before the down projection (fp32 accumulation).  Other y rows are
  * not touched.  Expects hy filled by twell_pack_gate_hybrid on the same
- * stream.  workspace: device, >= twell_ffn_hybrid_workspace_bytes(...),
- * 256-byte aligned, content ignored on entry. */
+ * stream.  workspace: device, >= twell_workspace_bytes(T, F, tile_w, cap,
+ * max_ovf, d, vdtype), 256-byte aligned, content ignored on entry. */
 TWELL_API int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
                        int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
@@ -197,8 +208,8 @@ TWELL_API int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const vo
  * (W_g^T and W_u^T tiles side by side) instead of two.
  *   x, wg_t, wu_t, wd : device, vdtype hy->ell.vdtype, 16-byte aligned;
  *   y : device [T][d] float; workspace: device, >=
- *   twell_ffn_hybrid_workspace_bytes(hy->max_ovf, F, d, vdtype), 256-byte
- *   aligned (may be NULL when that is 0), content ignored on entry.
+ *   twell_workspace_bytes(T, F, tile_w, cap, max_ovf, d, vdtype), 256-byte
+ *   aligned, content ignored on entry.
  *   Every check is made before the first launch. */
 TWELL_API int twell_ffn_forward(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
                       const twell_hybrid_t *hy, float *y, void *workspace, size_t workspace_bytes,

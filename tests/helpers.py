@@ -121,20 +121,20 @@ def run_hip(wl, max_ovf=None, stream=None, unaligned=False):
     y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
     yf = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
     yo = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
-    ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt)
+    ws = tw.hybrid_workspace(hy, wl.d)
     tw.twell_pack_gate_hybrid(x, wg, hy, stream)
     tw.twell_ffn_hybrid(hy, x, wu, wd, y, ws, stream)
-    tw.twell_ffn_fused(hy.ell, x, wu, wd, yf, stream)                 # ascending rows
-    tw.twell_ffn_fused(hy.ell, x, wu, wd, yo, stream, order=hy.order)  # work order
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, yf, ws, stream)                 # ascending rows
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, yo, ws, stream, order=hy.order)  # work order
     hy2 = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
     if unaligned:
         _offset_views(hy2, dt)
     y2 = _poison(hy2, wl.T, wl.d)
-    tw.twell_ffn_forward(x, wg, wu, wd, hy2, y2, tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt), stream)
+    tw.twell_ffn_forward(x, wg, wu, wd, hy2, y2, tw.hybrid_workspace(hy2, wl.d), stream)
     hy3 = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
     y3 = _poison(hy3, wl.T, wl.d)
     tw.twell_pack_gate(x, wg, hy3.ell, stream)
-    tw.twell_ffn_from_gate(x, wg, wu, wd, hy3, y3, tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt), stream)
+    tw.twell_ffn_from_gate(x, wg, wu, wd, hy3, y3, tw.hybrid_workspace(hy3, wl.d), stream)
     torch.cuda.synchronize()
     n_ovf = int(hy.n_ovf.item())
     m = min(n_ovf, max_ovf)

@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 107
+    assert lib.twell_version() == 200
 
 
 def test_status_strings():
@@ -83,16 +83,27 @@ def test_pack_gate_validation():
 def test_fused_and_hybrid_validation():
     lib = tw.load()
     d = _desc()
-    assert lib.twell_ffn_fused(ctypes.byref(d), None, GOOD, GOOD, GOOD, 64, None, None) == -1   # y NULL
-    assert lib.twell_ffn_fused(ctypes.byref(d), None, GOOD, GOOD, GOOD + 4, 64, GOOD, None) == -2
-    assert lib.twell_ffn_fused(ctypes.byref(d), None, GOOD, GOOD, GOOD, 60, GOOD, None) == -3
-    assert lib.twell_ffn_fused(ctypes.byref(d), GOOD + 2, GOOD, GOOD, GOOD, 64, GOOD, None) == -2  # order
+    need_f = lib.twell_workspace_bytes(16, 512, 128, 8, 0, 64, 1)
+    slots = 16 * 4 * 8                                                    # T * n_b * cap
+    # row entry counts (256 B here), each row's packed entries (neuron, gate value: 8 B per slot) and
+    # (d / 64) partial dot products per slot
+    assert need_f == 256 + slots * 8 + slots * 1 * 4
+    f = lib.twell_ffn_fused
+    r = ctypes.byref(d)
+    assert f(r, None, GOOD, GOOD, GOOD, 64, None, GOOD, need_f, None) == -1       # y NULL
+    assert f(r, None, GOOD, GOOD, GOOD + 4, 64, GOOD, GOOD, need_f, None) == -2
+    assert f(r, None, GOOD, GOOD, GOOD, 60, GOOD, GOOD, need_f, None) == -3
+    assert f(r, GOOD + 2, GOOD, GOOD, GOOD, 64, GOOD, GOOD, need_f, None) == -2   # order
+    assert f(r, None, GOOD, GOOD, GOOD, 64, GOOD, None, need_f, None) == -6       # no workspace
+    assert f(r, None, GOOD, GOOD, GOOD, 64, GOOD, GOOD, need_f - 1, None) == -6
+    assert f(r, None, GOOD, GOOD, GOOD, 64, GOOD, GOOD + 16, need_f, None) == -2  # workspace 256-aligned
     hy = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
-    need = lib.twell_ffn_hybrid_workspace_bytes(8, 512, 64, 1)
-    assert need > 0
+    need = lib.twell_workspace_bytes(16, 512, 128, 8, 8, 64, 1)
+    assert need > need_f
     assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, None, 0, None) == -6
     assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, GOOD, need - 1, None) == -6
     assert lib.twell_ffn_hybrid(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, GOOD + 16, need, None) == -2
+    assert lib.twell_ffn_overflow(ctypes.byref(hy), GOOD, GOOD, GOOD, 64, GOOD, GOOD, need - 1, None) == -6
     bad = tw.TwellHybridT(d, -1, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, ctypes.byref(bad), None) == -3
     nod = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, None, GOOD)
@@ -102,7 +113,12 @@ def test_fused_and_hybrid_validation():
     odd = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD + 2)             # order misaligned
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, ctypes.byref(odd), None) == -2
     assert lib.twell_partition_overflow(GOOD, GOOD, 64, None, None) == -1
-    assert lib.twell_ffn_hybrid_workspace_bytes(0, 512, 64, 1) == 0
+    # invalid sizes give 0
+    assert lib.twell_workspace_bytes(-1, 512, 128, 8, 0, 64, 1) == 0
+    assert lib.twell_workspace_bytes(16, 500, 128, 8, 0, 64, 1) == 0
+    assert lib.twell_workspace_bytes(16, 512, 100, 8, 0, 64, 1) == 0
+    assert lib.twell_workspace_bytes(16, 512, 128, 8, 0, 64, 2) == 0
+    assert lib.twell_workspace_bytes(0, 512, 128, 8, 0, 64, 1) == 0                # nothing to hold
 
 
 def test_ffn_forward_validation():
@@ -112,7 +128,7 @@ def test_ffn_forward_validation():
     d = _desc()
     hy = tw.TwellHybridT(d, 8, 0, GOOD, GOOD, GOOD, GOOD, GOOD)
     r = ctypes.byref(hy)
-    need = lib.twell_ffn_hybrid_workspace_bytes(8, 512, 64, 1)
+    need = lib.twell_workspace_bytes(16, 512, 128, 8, 8, 64, 1)
     assert f(GOOD, GOOD, GOOD, GOOD, 64, None, GOOD, GOOD, need, None) == -1          # hybrid NULL
     assert f(None, GOOD, GOOD, GOOD, 64, r, GOOD, GOOD, need, None) == -1             # x NULL
     assert f(GOOD, None, GOOD, GOOD, 64, r, GOOD, GOOD, need, None) == -1             # W_g NULL

@@ -109,8 +109,8 @@ def test_batch_step_graph_replay(gpu_lib):
     dt, x, wg, wu, wd = to_device(wl)
     hy = tw.Hybrid.empty(T, wl.F, wl.tile_w, wl.cap, dt, T)
     hy_e = tw.Hybrid.empty(T, wl.F, wl.tile_w, wl.cap, dt, T)
-    ws = tw.hybrid_workspace(T, wl.F, wl.d, dt)
-    ws_e = tw.hybrid_workspace(T, wl.F, wl.d, dt)
+    ws = tw.hybrid_workspace(hy, wl.d)
+    ws_e = tw.hybrid_workspace(hy_e, wl.d)
     y = torch.empty((T, wl.d), dtype=torch.float32, device="cuda")
     y_e = torch.empty_like(y)
 

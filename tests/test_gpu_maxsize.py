@@ -43,7 +43,7 @@ def test_max_rows_layer_2b(gpu_lib):
     x = x0.repeat((T + B - 1) // B, 1)[:T]
     assert x.is_contiguous()
     hy = tw.Hybrid.empty(T, base.F, base.tile_w, base.cap, dt, max_ovf)
-    ws = tw.hybrid_workspace(max_ovf, base.F, base.d, dt)
+    ws = tw.hybrid_workspace(hy, base.d)
     y = torch.full((T, base.d), float("nan"), dtype=torch.float32, device="cuda")
     hy.ell.cnt.fill_(-7)
     hy.n_ovf.fill_(-7)

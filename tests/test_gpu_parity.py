@@ -206,8 +206,9 @@ def test_fused_order_out_of_range(gpu_lib):
     order[1] = wl.T + 5
     y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
     yref = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
-    tw.twell_ffn_fused(hy.ell, x, wu, wd, y, order=order)
-    tw.twell_ffn_fused(hy.ell, x, wu, wd, yref)
+    ws = tw.hybrid_workspace(hy, wl.d)
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, y, ws, order=order)
+    tw.twell_ffn_fused(hy.ell, x, wu, wd, yref, ws)
     torch.cuda.synchronize()
     y, yref = y.cpu().numpy(), yref.cpu().numpy()
     np.testing.assert_array_equal(y[0::2], yref[0::2])

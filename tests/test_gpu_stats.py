@@ -133,7 +133,7 @@ def test_stats_gate_then_from_gate(gpu_lib, name):
     for with_stats in (False, True):
         hy = tw.Hybrid.empty(wl.T, wl.F, wl.tile_w, wl.cap, dt, max_ovf)
         y = torch.full((wl.T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
-        ws = tw.hybrid_workspace(max_ovf, wl.F, wl.d, dt)
+        ws = tw.hybrid_workspace(hy, wl.d)
         if with_stats:
             ncnt = torch.zeros(wl.F, dtype=torch.int32, device="cuda")
             l1 = torch.empty((wl.T, n_b), dtype=torch.float32, device="cuda")

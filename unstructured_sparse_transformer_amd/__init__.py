@@ -9,7 +9,7 @@ The functions carry the C names (``include/twell.h``):
 ``twell_ffn_forward``, ``twell_ffn_from_gate``, ``twell_pack_gate``, ``twell_pack_gate_stats``, ``twell_partition_overflow``,
 ``twell_pack_gate_hybrid``,
 ``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
-``twell_ffn_hybrid_workspace_bytes``, ``twell_ffn_decode``,
+``twell_workspace_bytes``, ``twell_ffn_decode``,
 ``twell_ffn_decode_workspace_bytes``, ``twell_ffn_decode_noalloc``, ``twell_dense_to_hybrid``,
 ``twell_hybrid_to_dense``, ``twell_compact_min_bytes``, ``twell_compact_hybrid``,
 ``twell_compact_to_dense``, ``twell_ffn_backward``,
@@ -20,7 +20,7 @@ all contiguous on the GPU; y [T][d] fp32)::
 
     import unstructured_sparse_transformer_amd as tw
     hy = tw.Hybrid.empty(T, F, tile_w=256, cap=16, dtype=torch.bfloat16, max_ovf=1024)
-    ws = tw.hybrid_workspace(1024, F, d, torch.bfloat16)
+    ws = tw.hybrid_workspace(hy, d)
     tw.twell_ffn_forward(x, wg_t, wu_t, wd, hy, y, ws)   # on the current stream
     # hy.ell holds the TwELL of ReLU(x W_g); hy.n_ovf counts the overflow rows.
     # Overflow rows past max_ovf are counted but not computed: after
@@ -43,7 +43,7 @@ TWELL_F32, TWELL_BF16 = 0, 1
 STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_SHAPE",
           -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE", -7: "TWELL_E_SCRATCH"}
 EXPORTS = ("twell_ffn_forward", "twell_ffn_from_gate", "twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
-           "twell_ffn_fused", "twell_ffn_hybrid_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
+           "twell_ffn_fused", "twell_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
            "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_ffn_decode_noalloc", "twell_dense_to_hybrid", "twell_hybrid_to_dense",
            "twell_compact_min_bytes", "twell_compact_hybrid", "twell_compact_to_dense",
            "twell_ffn_backward_workspace_bytes", "twell_ffn_backward", "twell_status_str", "twell_version")
@@ -85,9 +85,9 @@ def load(path: str = LIB_PATH):
     lib.twell_pack_gate_stats.argtypes = [P, P, I32, ctypes.POINTER(TwellT), P, P, P]
     lib.twell_partition_overflow.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
     lib.twell_pack_gate_hybrid.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
-    lib.twell_ffn_fused.argtypes = [ctypes.POINTER(TwellT), P, P, P, P, I32, P, P]
-    lib.twell_ffn_hybrid_workspace_bytes.argtypes = [I32, I32, I32, I32]
-    lib.twell_ffn_hybrid_workspace_bytes.restype = ctypes.c_size_t
+    lib.twell_ffn_fused.argtypes = [ctypes.POINTER(TwellT), P, P, P, P, I32, P, P, ctypes.c_size_t, P]
+    lib.twell_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.twell_workspace_bytes.restype = ctypes.c_size_t
     lib.twell_ffn_hybrid.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
     lib.twell_ffn_overflow.argtypes = [ctypes.POINTER(TwellHybridT), P, P, P, I32, P, P, ctypes.c_size_t, P]
     lib.twell_ffn_forward.argtypes = [P, P, P, P, I32, ctypes.POINTER(TwellHybridT), P, P, ctypes.c_size_t, P]
@@ -230,14 +230,16 @@ def twell_pack_gate_hybrid(x, wg_t, hy: Hybrid, stream=None):
                                       _stream(stream)))
 
 
-def twell_ffn_fused(tw: TwELL, x, wu_t, wd, y, stream=None, order=None):
+def twell_ffn_fused(tw: TwELL, x, wu_t, wd, y, workspace, stream=None, order=None):
     lib = load()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("twell_ffn_fused", lib.twell_ffn_fused(ctypes.byref(tw.desc()), _ptr(order), _ptr(x), _ptr(wu_t),
-                                                  _ptr(wd), int(x.shape[1]), _ptr(y), _stream(stream)))
+                                                  _ptr(wd), int(x.shape[1]), _ptr(y), _ptr(workspace), nbytes,
+                                                  _stream(stream)))
 
 
-def twell_ffn_hybrid_workspace_bytes(max_ovf: int, F: int, d: int, dtype) -> int:
-    return int(load().twell_ffn_hybrid_workspace_bytes(max_ovf, F, d, vdtype_of(dtype)))
+def twell_workspace_bytes(T: int, F: int, tile_w: int, cap: int, max_ovf: int, d: int, dtype) -> int:
+    return int(load().twell_workspace_bytes(T, F, tile_w, cap, max_ovf, d, vdtype_of(dtype)))
 
 
 def twell_ffn_hybrid(hy: Hybrid, x, wu_t, wd, y, workspace, stream=None):
@@ -363,8 +365,16 @@ def decode_workspace(T: int, F: int, d: int, tile_w: int, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def hybrid_workspace(max_ovf: int, F: int, d: int, dtype, device="cuda"):
-    """A workspace tensor of the size twell_ffn_hybrid needs (256-byte aligned by the allocator)."""
+def workspace(T: int, F: int, tile_w: int, cap: int, max_ovf: int, d: int, dtype, device="cuda"):
+    """A workspace tensor of the size twell_workspace_bytes gives (256-byte
+    aligned by the allocator); it serves twell_ffn_fused, twell_ffn_overflow,
+    twell_ffn_hybrid, twell_ffn_forward and twell_ffn_from_gate."""
     import torch
-    n = twell_ffn_hybrid_workspace_bytes(max_ovf, F, d, dtype)
+    n = twell_workspace_bytes(T, F, tile_w, cap, max_ovf, d, dtype)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def hybrid_workspace(hy: "Hybrid", d: int, device="cuda"):
+    """The workspace for the calls on hybrid `hy` with model width d."""
+    e = hy.ell
+    return workspace(e.T, e.F, e.tile_w, e.cap, hy.max_ovf, d, e.dtype, device)

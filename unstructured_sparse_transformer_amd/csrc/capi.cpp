@@ -88,10 +88,45 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_E_HIP; 
             return _st;                  \
     } while (0)
 
-size_t hybrid_ws_p_bytes(int32_t max_ovf, int32_t F, int32_t vdtype)
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace of the calls that take one (the fused step and the overflow FFN),
+// 256-byte aligned sections: the fused step's (twell::fused_ws_layout: packed
+// entries, entry counts, partial dot products), the overflow rows' gated
+// products [max_ovf][F] (vdtype), and the down projection's split-K partial
+// slabs [splits][max_ovf][d] fp32.
+struct Ws {
+    size_t s_off, p_off, part_off, bytes;
+    int splits;
+};
+
+Ws ws_layout(int32_t T, int32_t F, int32_t tile_w, int32_t cap, int32_t max_ovf, int32_t d, int32_t vdtype)
 {
-    const size_t b = (size_t)max_ovf * (size_t)F * (size_t)elem_size(vdtype);
-    return (b + 255) & ~(size_t)255;
+    Ws w{};
+    w.s_off = 0;
+    w.p_off = up256(twell::fused_ws_layout(nullptr, T, F, tile_w, cap, d, elem_size(vdtype)).bytes);
+    w.splits = max_ovf > 0 ? twell::down_splits(max_ovf, F, d) : 1;
+    w.part_off = w.p_off + (max_ovf > 0 ? up256((size_t)max_ovf * (size_t)F * (size_t)elem_size(vdtype)) : 0);
+    w.bytes = w.part_off + (max_ovf > 0 && w.splits > 1 ? (size_t)w.splits * max_ovf * d * sizeof(float) : 0);
+    return w;
+}
+
+Ws ws_layout(const twell_hybrid_t *hy, int32_t d)
+{
+    const twell_t *h = &hy->ell;
+    return ws_layout(h->T, h->F, h->tile_w, h->cap, hy->max_ovf, d, h->vdtype);
+}
+
+// The workspace argument against a layout's size.
+int check_ws(const void *workspace, size_t workspace_bytes, size_t need)
+{
+    if (need == 0)
+        return TWELL_OK;
+    if (!workspace || workspace_bytes < need)
+        return TWELL_E_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return TWELL_E_ALIGN;
+    return TWELL_OK;
 }
 
 // Checks shared by twell_ffn_from_gate and twell_ffn_forward (T > 0).
@@ -105,38 +140,34 @@ int check_layer(const void *x, const void *wg_t, const void *wu_t, const void *w
     TWELL_TRY(check_mat(wu_t));
     TWELL_TRY(check_mat(wd));
     TWELL_TRY(check_mat(y));
-    const size_t need = twell_ffn_hybrid_workspace_bytes(hy->max_ovf, h->F, d, h->vdtype);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return TWELL_E_WORKSPACE;
-    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return TWELL_E_ALIGN;
-    return TWELL_OK;
+    return check_ws(workspace, workspace_bytes, ws_layout(hy, d).bytes);
 }
 
-// The layer after the gate, arguments already checked: overflow flags,
-// overflow list and work order, the fused step, then the dense backup and
-// gated up product of the overflow rows in one GEMM, and their down projection.
+// The layer after the gate, arguments already checked: the fused step's
+// entries kernel (which also writes the overflow flags and work values), the
+// overflow list and work order, the fused step's two passes, then the dense
+// backup and gated up product of the overflow rows in one GEMM, and their
+// down projection.
 int launch_from_gate(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
                      const twell_hybrid_t *hy, float *y, void *workspace, hipStream_t s)
 {
     const twell_t *h = &hy->ell;
-    const int n_b = h->F / h->tile_w;
-    TWELL_TRY(hip_status(twell::launch_row_flags(h->cnt, h->T, n_b, h->cap, hy->row_ovf, hy->order, s)));
+    const Ws w = ws_layout(hy, d);
+    char *ws = static_cast<char *>(workspace);
+    TWELL_TRY(hip_status(twell::launch_ffn_entries(h->vdtype, h->cnt, h->val, h->idx, h->T, h->F, h->tile_w, h->cap,
+                                                   d, ws + w.s_off, hy->row_ovf, hy->order, s)));
     TWELL_TRY(hip_status(
         twell::launch_compact_rows(hy->row_ovf, h->T, hy->max_ovf, hy->ovf_rows, hy->n_ovf, hy->order, s)));
-    TWELL_TRY(hip_status(twell::launch_ffn_fused(h->vdtype, h->cnt, h->val, h->idx, hy->order, h->T, h->F,
-                                                 h->tile_w, h->cap, x, wu_t, wd, d, y, s)));
+    TWELL_TRY(hip_status(twell::launch_ffn_passes(h->vdtype, h->cnt, h->val, h->idx, hy->order, h->T, h->F,
+                                                  h->tile_w, h->cap, x, wu_t, wd, d, y, ws + w.s_off, s)));
     if (hy->max_ovf == 0)
         return TWELL_OK;
-    char *ws = static_cast<char *>(workspace);
-    void *pbuf = ws;
-    const int splits = twell::down_splits(hy->max_ovf, h->F, d);
-    float *part = splits > 1 ? reinterpret_cast<float *>(ws + hybrid_ws_p_bytes(hy->max_ovf, h->F, h->vdtype))
-                             : nullptr;
+    void *pbuf = ws + w.p_off;
+    float *part = w.splits > 1 ? reinterpret_cast<float *>(ws + w.part_off) : nullptr;
     TWELL_TRY(hip_status(twell::launch_dense_gate_up(h->vdtype, x, h->T, wg_t, wu_t, hy->ovf_rows, hy->n_ovf,
                                                      hy->max_ovf, d, h->F, hy->dense, pbuf, s)));
     return hip_status(twell::launch_down(h->vdtype, pbuf, wd, hy->ovf_rows, hy->n_ovf, hy->max_ovf, h->F, d, y, part,
-                                         splits, s));
+                                         w.splits, s));
 }
 
 // Checks of the decode-shaped calls, apart from their workspace (T == 0
@@ -178,7 +209,7 @@ int launch_decode(const void *x, const void *wg_t, const void *wu_t, const void 
 
 extern "C" {
 
-int twell_version(void) { return 107; }
+int twell_version(void) { return 200; }
 
 const char *twell_status_str(int status)
 {
@@ -460,7 +491,7 @@ int twell_ffn_decode_noalloc(const void *x, const void *wg_t, const void *wu_t, 
 }
 
 int twell_ffn_fused(const twell_t *h, const int32_t *order, const void *x, const void *wu_t, const void *wd,
-                    int32_t d, float *y, void *stream)
+                    int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream)
 {
     TWELL_TRY(check_layout(h, d));
     if (h->T == 0)
@@ -472,19 +503,21 @@ int twell_ffn_fused(const twell_t *h, const int32_t *order, const void *x, const
     TWELL_TRY(check_mat(y));
     if (reinterpret_cast<uintptr_t>(order) & 3u)
         return TWELL_E_ALIGN;
+    const Ws w = ws_layout(h->T, h->F, h->tile_w, h->cap, 0, d, h->vdtype);
+    TWELL_TRY(check_ws(workspace, workspace_bytes, w.bytes));
     return hip_status(twell::launch_ffn_fused(h->vdtype, h->cnt, h->val, h->idx, order, h->T, h->F, h->tile_w,
-                                              h->cap, x, wu_t, wd, d, y, static_cast<hipStream_t>(stream)));
+                                              h->cap, x, wu_t, wd, d, y, static_cast<char *>(workspace) + w.s_off,
+                                              static_cast<hipStream_t>(stream)));
 }
 
-size_t twell_ffn_hybrid_workspace_bytes(int32_t max_ovf, int32_t F, int32_t d, int32_t vdtype)
+size_t twell_workspace_bytes(int32_t T, int32_t F, int32_t tile_w, int32_t cap, int32_t max_ovf, int32_t d,
+                             int32_t vdtype)
 {
-    if (max_ovf <= 0 || F <= 0 || d <= 0)
+    if (T < 0 || F <= 0 || d <= 0 || max_ovf < 0 || cap < 1 || (tile_w != 32 && tile_w != 64 && tile_w != 128 &&
+                                                                 tile_w != 256) || F % tile_w != 0 ||
+        (vdtype != TWELL_F32 && vdtype != TWELL_BF16))
         return 0;
-    const int splits = twell::down_splits(max_ovf, F, d);
-    size_t b = hybrid_ws_p_bytes(max_ovf, F, vdtype);
-    if (splits > 1)
-        b += (size_t)splits * (size_t)max_ovf * (size_t)d * sizeof(float);
-    return b;
+    return ws_layout(T, F, tile_w, cap, max_ovf, d, vdtype).bytes;
 }
 
 int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd, int32_t d,
@@ -501,21 +534,16 @@ int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const void *wu_t
     TWELL_TRY(check_mat(wu_t));
     TWELL_TRY(check_mat(wd));
     TWELL_TRY(check_mat(y));
-    const size_t need = twell_ffn_hybrid_workspace_bytes(hy->max_ovf, h->F, d, h->vdtype);
-    if (!workspace || workspace_bytes < need)
-        return TWELL_E_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return TWELL_E_ALIGN;
+    const Ws w = ws_layout(hy, d);
+    TWELL_TRY(check_ws(workspace, workspace_bytes, w.bytes));
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
-    void *pbuf = ws;
-    const int splits = twell::down_splits(hy->max_ovf, h->F, d);
-    float *part = splits > 1 ? reinterpret_cast<float *>(ws + hybrid_ws_p_bytes(hy->max_ovf, h->F, h->vdtype))
-                             : nullptr;
+    void *pbuf = ws + w.p_off;
+    float *part = w.splits > 1 ? reinterpret_cast<float *>(ws + w.part_off) : nullptr;
     TWELL_TRY(hip_status(twell::launch_gated_up(h->vdtype, x, h->T, wu_t, hy->ovf_rows, hy->n_ovf, hy->max_ovf, d, h->F,
                                                 hy->dense, pbuf, s)));
     return hip_status(twell::launch_down(h->vdtype, pbuf, wd, hy->ovf_rows, hy->n_ovf, hy->max_ovf, h->F, d, y, part,
-                                         splits, s));
+                                         w.splits, s));
 }
 
 int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd, int32_t d, float *y,
@@ -528,12 +556,8 @@ int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, 
     TWELL_TRY(check_hybrid(hy));
     if (h->T == 0)
         return TWELL_OK;
-    const size_t need = twell_ffn_hybrid_workspace_bytes(hy->max_ovf, h->F, d, h->vdtype);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return TWELL_E_WORKSPACE;
-    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return TWELL_E_ALIGN;
-    TWELL_TRY(twell_ffn_fused(h, hy->order, x, wu_t, wd, d, y, stream));
+    TWELL_TRY(check_ws(workspace, workspace_bytes, ws_layout(hy, d).bytes));
+    TWELL_TRY(twell_ffn_fused(h, hy->order, x, wu_t, wd, d, y, workspace, workspace_bytes, stream));
     return twell_ffn_overflow(hy, x, wu_t, wd, d, y, workspace, workspace_bytes, stream);
 }
 

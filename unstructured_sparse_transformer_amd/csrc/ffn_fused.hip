@@ -2,41 +2,25 @@
 //
 // "Sparser, Faster, Lighter Transformer Language Models" (gist.science
 // summary), section 2.2: with the gate activation h_g in TwELL, the up and
-// down projections become one kernel that, for each nonzero h_g[j], reads
+// down projections become one step that, for each nonzero h_g[j], reads
 // only the weights it needs (column j of W_u, row j of W_d), takes a dot
 // product and a scalar product, and accumulates -- DRAM traffic is the point.
 //
-// gfx950 mapping: one workgroup of 4 waves per token, started in a given
-// work order (tokens with the most entries first, so that they do not trail
-// at the end of the launch while the light ones have long finished).  Each wave keeps the
-// token's x row and a partial y row in registers (chunk c of lane l covers
-// elements (l + 64c)*E .. +E, so every weight-row read is one fully coalesced
-// 16-byte-per-lane sweep).  The token's TwELL entries are compacted into an LDS
-// list of (j, h) in ascending j (wave prefix sum over the per-tile counts) and
-// dealt to the waves G at a time (G = 1), so heavy tokens (hundreds of
-// entries) run 4 latency chains in parallel; the next group's 2*G weight rows
-// are in flight while a wave reduces the current one, the dot products are
-// reduced with DPP, and y += (h*u) * W_d[j] runs in fp32.
-// The partial rows are added in LDS in a fixed order: no atomics, and the
-// result does not depend on timing.
+// gfx950 mapping (batch path): two passes, each arranged so that one XCD
+// gathers only weight rows that fit its L2 (see "batch path" below); every
+// weight row, x row and partial sum is moved with 16-byte-per-lane coalesced
+// loads, dot products are reduced with DPP, and all sums run in a fixed order
+// (no atomics), so the result does not depend on timing.  The decode path
+// (T <= 64) keeps one wave per chunk of a row's entries, with both weight
+// rows of an entry in registers (group_load / group_apply below).
+#include <algorithm>
+
 #include "decode.h"
 #include "launch.h"
 #include "twell_device.h"
 #include "wave_ops.h"
 
-// Entries per group (G).  One entry per group keeps the 2B-shaped kernel at
-// 166 VGPRs: three waves per SIMD, three tokens per CU in flight (two at
-// G = 2, 234 VGPRs), which the latency-bound light and empty rows need.
-#ifndef FUSED_G
-#define FUSED_G 1
-#endif
-
 namespace twell {
-
-#ifndef FUSED_WAVES
-#define FUSED_WAVES 4
-#endif
-constexpr int NWV = FUSED_WAVES;  // waves per token
 
 // The token's x row as this lane's chunks in fp32 registers.
 template <typename TI, int NC> struct XRow {
@@ -146,82 +130,87 @@ __device__ __forceinline__ void group_stream(const FusedArgs<TI> &a, const int2 
     }
 }
 
-// One workgroup of NWV waves per token.  Wave w owns the TwELL tiles
-// b = w, w + NWV, w + 2 NWV, ...: it reads their counts, indices and values
-// itself, compacts its entries (ascending tile, then slot) into a private LDS
-// list of at most WLIST entries at a time, and streams them G at a time.  No
-// barrier is needed until the NWV partial y rows meet in LDS, where every wave
-// adds a quarter of the columns in wave order.  Tokens without entries and
-// overflow rows get y = 0.
-constexpr int WLIST = 128;  // entries per wave per pass
+// ------------------------------------------------------------------ batch path
+// Three kernels.
+//
+// Entries (ffn_entries_kernel), one wave per row t: the row's stored entries
+// (j, h) in ascending (tile, slot) order, packed at the start of the row's own
+// range of TwELL slots (ent[t n_b cap + k], k < e_t), and e_t (0 for an
+// overflow row), so that the passes below need one round of dependent loads
+// per row instead of reading counts, then indices and values, per column
+// slice.  In the one-call path it also writes the overflow flag and work value
+// (row_ovf, work) the partition's compaction reads.
+//
+// Up and down passes (ffn_pass_kernel), split over the columns of d: a
+// workgroup serves one column slice [c cw, (c + 1) cw) (cw = d / nch, nch = 8
+// column slices at the usual widths), and workgroups are handed to the 8 XCDs
+// round-robin (workgroup g runs on XCD g % 8), so XCD c only ever reads
+// column slice c of x, W_u^T and W_d: the live rows' slices of one weight
+// matrix (3.4 MB at the 2B shape) stay in its 4 MB L2.  A row slice is LPE
+// 16-byte pieces; a wave serves 64 / LPE rows (consecutive work positions),
+// one per group of LPE lanes, each lane one piece, and the groups step through
+// their rows' entries together.  The up pass keeps the lane's piece of x[t] in
+// registers and writes, per entry, the partial dot product of x[t] and
+// W_u^T[j] over the slice (DPP reduction over the group's lanes) to
+// p[slot][c] (fp32).  The down pass forms s = h * (p[slot][0] + ... +
+// p[slot][nch - 1]) (fixed order) and accumulates y[t][slice] += s * W_d[j]
+// in the lanes' registers, in ascending entry order.  Every value comes from
+// one lane group in a fixed order, so the result does not depend on timing.
+// Overflow rows, and rows without entries, get y = 0 (the dense path writes
+// the overflow rows afterwards).
+template <typename TI> struct PassArgs {
+    const int32_t *cnt;
+    const TI *val;
+    const uint8_t *idx;
+    const int32_t *order;  // row of work position i (null: row i)
+    int T, n_b, tile_w, cap, F;
+    const TI *x, *wu_t, *wd;
+    int d;
+    FusedWs w;
+    float *y;
+    int cw;                   // width of a column slice (d = w.nch * cw)
+    int32_t *row_ovf, *work;  // optional (one-call path): overflow flag, work value
+};
 
-template <typename TI, int NC, int G>
-__global__ __launch_bounds__(64 * NWV) void ffn_fused_kernel(FusedArgs<TI> a)
+constexpr int PASS_WAVES = 4;
+#ifndef PASS_STEPS
+#define PASS_STEPS 4
+#endif
+#ifndef PASS_PREFETCH
+#define PASS_PREFETCH 1
+#endif
+constexpr int PASS_U = PASS_STEPS;  // entry steps in flight per lane
+
+template <typename TI>
+__global__ __launch_bounds__(64 * PASS_WAVES) void ffn_entries_kernel(PassArgs<TI> a)
 {
     constexpr int E = Elt<TI>::PER_CHUNK;
-    constexpr int YW = NC * 64 * E;  // floats of one partial y row (>= d)
-    __shared__ int2 wlist[NWV][WLIST];
-    __shared__ __attribute__((aligned(16))) float part[NWV][YW];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int t = blockIdx.x;
-    if (a.order) {
-        t = a.order[t];
-        if ((unsigned)t >= (unsigned)a.T)
-            return;  // not a permutation: this row is not ours to write
-    }
-    const int64_t row_bytes = (int64_t)a.d * Elt<TI>::SIZE;
-    float *yrow = a.y + (int64_t)t * a.d;
-
-    // Overflow test over the whole row (every wave, same answer).
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * PASS_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (t >= a.T)
+        return;
     const int32_t *crow = a.cnt + (int64_t)t * a.n_b;
     bool ovf = false;
-    int total = 0;
     for (int b0 = 0; b0 < a.n_b; b0 += 64) {
         const int b = b0 + lane;
-        const int c = b < a.n_b ? crow[b] : 0;
-        ovf |= __ballot(c > a.cap) != 0ull;
-        total += wave_isum(c < a.cap ? c : a.cap);
+        ovf |= __ballot(b < a.n_b && crow[b] > a.cap) != 0ull;
     }
-    if (ovf || total == 0) {
-        for (int i = tid * 4; i < a.d; i += 64 * NWV * 4)
-            *reinterpret_cast<float4 *>(yrow + i) = make_float4(0.f, 0.f, 0.f, 0.f);
-        return;
-    }
-
-    XRow<TI, NC> xf;
-    float yacc[NC][E];
-    const char *xrow = (const char *)a.x + (int64_t)t * row_bytes;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            yacc[c][e] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int ch = lane + 64 * c;
-        xf.set(c, ch < a.nchunks ? ldg16(xrow + ch * 16) : u32x4{0, 0, 0, 0});
-    }
-
-    // This wave's tiles: b = wave + NWV * l for l = 0, 1, ...; lane l holds tile l.
-    const int my_tiles = (a.n_b - wave + NWV - 1) / NWV;
-    const bool vec = a.cap % 16 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 15u) == 0 &&
-                     (reinterpret_cast<uintptr_t>(a.val) & 15u) == 0;
-    int2 *list = wlist[wave];
-    for (int l0 = 0; l0 < my_tiles; l0 += 64) {
-        const int l = l0 + lane;
-        const int b = wave + NWV * l;
-        int c = l < my_tiles ? crow[b] : 0;
-        c = c < a.cap ? c : a.cap;
-        const int incl = wave_incl_scan(c, lane);
-        const int ctot = __shfl(incl, 63, 64);
-        const int64_t slot0 = ((int64_t)t * a.n_b + b) * a.cap;
-        for (int win = 0; win < ctot; win += WLIST) {
-            const int excl = incl - c - win;  // position of this tile's first entry in the window
+    const int64_t rbase = (int64_t)t * a.n_b * a.cap;
+    int2 *erow = a.w.ent + rbase;
+    int run = 0;
+    if (!ovf) {
+        const bool vec = a.cap % 16 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 15u) == 0 &&
+                         (reinterpret_cast<uintptr_t>(a.val) & 15u) == 0;
+        for (int b0 = 0; b0 < a.n_b; b0 += 64) {
+            const int b = b0 + lane;
+            int c = b < a.n_b ? crow[b] : 0;
+            c = c < a.cap ? c : a.cap;
+            const int incl = wave_incl_scan(c, lane);
+            const int excl = run + incl - c;
+            run += __shfl(incl, 63, 64);
+            const int64_t slot0 = rbase + (int64_t)b * a.cap;
             if (vec) {
                 for (int s0 = 0; s0 < c; s0 += 16) {
-                    if (excl + s0 >= WLIST || excl + s0 + 16 <= 0)
-                        continue;
                     const u32x4 iw = ldg16(a.idx + slot0 + s0);
                     u32x4 vw[16 / E];
 #pragma unroll
@@ -229,95 +218,343 @@ __global__ __launch_bounds__(64 * NWV) void ffn_fused_kernel(FusedArgs<TI> a)
                         vw[q] = ldg16(a.val + slot0 + s0 + q * E);
 #pragma unroll
                     for (int k = 0; k < 16; ++k) {
-                        const int pos = excl + s0 + k;
-                        if (s0 + k < c && pos >= 0 && pos < WLIST) {
+                        if (s0 + k < c) {
                             int j = b * a.tile_w + (int)((iw[k >> 2] >> (8 * (k & 3))) & 0xFFu);
                             j = j < a.F ? j : a.F - 1;  // memory safety for a corrupt index
-                            list[pos] = make_int2(j, __float_as_int(chunk_elem<TI>(vw[k / E], k % E)));
+                            erow[excl + s0 + k] = make_int2(j, __float_as_int(chunk_elem<TI>(vw[k / E], k % E)));
                         }
                     }
                 }
             } else {
                 for (int s = 0; s < c; ++s) {
-                    const int pos = excl + s;
-                    if (pos >= 0 && pos < WLIST) {
-                        int j = b * a.tile_w + a.idx[slot0 + s];
-                        j = j < a.F ? j : a.F - 1;  // memory safety for a corrupt index
-                        list[pos] = make_int2(j, __float_as_int(load_elem(a.val + slot0 + s)));
+                    int j = b * a.tile_w + a.idx[slot0 + s];
+                    j = j < a.F ? j : a.F - 1;  // memory safety for a corrupt index
+                    erow[excl + s] = make_int2(j, __float_as_int(load_elem(a.val + slot0 + s)));
+                }
+            }
+        }
+    }
+    if (lane == 0) {
+        a.w.row_e[t] = run;
+        if (a.row_ovf) {
+            a.row_ovf[t] = ovf;
+            a.work[t] = run;
+        }
+    }
+}
+
+// Sum of v over each aligned group of L lanes (L = 8, 16, 32, 64), left in
+// the group's last lane (DPP row shifts, then row broadcasts).
+template <int L> __device__ __forceinline__ float group_sum_last(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));  // row_shr:1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));  // row_shr:2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));  // row_shr:4
+    if (L >= 16)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));  // row_shr:8
+    if (L >= 32)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));  // row_bcast:15
+    if (L >= 64)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return v;
+}
+
+// One row's window of up to 64 entries (k = w0 + lane), as (j, payload):
+// up pass payload = slot; down pass payload = s = h * (sum of the entry's
+// partial dot products).  x piece: the up pass's lane piece of x[t].
+template <typename TI, bool DOWN> struct RowWin {
+    int2 en;
+    float pv[DOWN ? 8 : 1];
+    u32x4 xv;
+};
+
+template <typename TI, bool DOWN>
+__device__ __forceinline__ void row_win_load(const PassArgs<TI> &a, int t, int e, int w0, int lane, int64_t col_off,
+                                             RowWin<TI, DOWN> &r)
+{
+    const int slots = a.n_b * a.cap;
+    const int64_t rbase = (int64_t)t * slots;
+    const int k = w0 + lane;
+    const bool ok = k < e;
+    r.en = ok ? a.w.ent[rbase + k] : make_int2(0, 0);
+    if (DOWN) {
+        if (a.w.nch == 8) {
+            const float4 q0 = ok ? *reinterpret_cast<const float4 *>(a.w.p + (rbase + k) * 8) : make_float4(0, 0, 0, 0);
+            const float4 q1 = ok ? *reinterpret_cast<const float4 *>(a.w.p + (rbase + k) * 8 + 4) : make_float4(0, 0, 0, 0);
+            r.pv[0] = q0.x; r.pv[1] = q0.y; r.pv[2] = q0.z; r.pv[3] = q0.w;
+            r.pv[4] = q1.x; r.pv[5] = q1.y; r.pv[6] = q1.z; r.pv[7] = q1.w;
+        }
+    } else if (w0 == 0) {
+        r.xv = ldg16((const char *)a.x + (int64_t)t * a.d * Elt<TI>::SIZE + col_off);
+    }
+}
+
+#ifndef PASS_NROWS
+#define PASS_NROWS 2
+#endif
+constexpr int PASS_ROWS = PASS_NROWS;  // consecutive work positions per wave
+
+template <typename TI, int LPE, bool DOWN>
+__global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> a)
+{
+    constexpr int E = Elt<TI>::PER_CHUNK;  // elements per 16-byte piece
+    constexpr int EPI = 64 / LPE;          // entries per step
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nch = a.w.nch;
+    const int csl = blockIdx.x % nch;
+    // the wave's rows: work positions w, w + W, w + 2 W, ... (W waves per
+    // slice), so that the heaviest rows, which lead the work order, land in
+    // different waves; lane r < PASS_ROWS holds row r and its entry count
+    const int nwv = (a.T + PASS_ROWS - 1) / PASS_ROWS;
+    const int wv0 = (blockIdx.x / nch) * PASS_WAVES + wave;
+    if (wv0 >= nwv)
+        return;
+    const int ip = wv0 + lane * nwv;
+    int tv = -1, ev = 0;
+    if (lane < PASS_ROWS && ip < a.T) {
+        tv = a.order ? a.order[ip] : ip;
+        tv = (unsigned)tv < (unsigned)a.T ? tv : -1;  // not a permutation: not ours to write
+    }
+    if (tv >= 0)
+        ev = a.w.row_e[tv];
+    // row r of the wave: tr(r), er(r) (scalar reads of lane r)
+#define tr(r) __builtin_amdgcn_readlane(tv, (r))
+#define er(r) __builtin_amdgcn_readlane(ev, (r))
+    const int q = lane / LPE, pc = lane % LPE;  // entry of the step, 16-byte piece of the row slice
+    const int64_t row_bytes = (int64_t)a.d * Elt<TI>::SIZE;
+    const int64_t col_off = (int64_t)(csl * a.cw + pc * E) * Elt<TI>::SIZE;
+    const char *wbase = (const char *)(DOWN ? a.wd : a.wu_t) + col_off;
+    const int slots = a.n_b * a.cap;
+    // first row with entries, its first window requested at once
+    int r = 0;
+    while (r < PASS_ROWS && (tr(r) < 0 || er(r) == 0)) {
+        if (DOWN && tr(r) >= 0 && er(r) == 0) {
+            float *yrow = a.y + (int64_t)tr(r) * a.d + csl * a.cw;
+            for (int k = lane * 4; k < a.cw; k += 256)
+                *reinterpret_cast<float4 *>(yrow + k) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        ++r;
+    }
+    if (r == PASS_ROWS)
+        return;
+    RowWin<TI, DOWN> cur;
+    row_win_load<TI, DOWN>(a, tr(r), er(r), 0, lane, col_off, cur);
+    while (r < PASS_ROWS) {
+        const int t = tr(r), e = er(r);
+        const int64_t rbase = (int64_t)t * slots;
+        float xf[E], acc[E];
+        if (!DOWN) {
+#pragma unroll
+            for (int e2 = 0; e2 < E; ++e2)
+                xf[e2] = chunk_elem<TI>(cur.xv, e2);
+        }
+#pragma unroll
+        for (int e2 = 0; e2 < E; ++e2)
+            acc[e2] = 0.f;
+        // the next row with entries (zero-filling the empty ones on the way, down pass)
+        int rn = r + 1;
+        while (rn < PASS_ROWS && (tr(rn) < 0 || er(rn) == 0)) {
+            if (DOWN && tr(rn) >= 0 && er(rn) == 0) {
+                float *yrow = a.y + (int64_t)tr(rn) * a.d + csl * a.cw;
+                for (int k = lane * 4; k < a.cw; k += 256)
+                    *reinterpret_cast<float4 *>(yrow + k) = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            ++rn;
+        }
+        for (int w0 = 0; w0 < e; w0 += 64) {
+            if (w0 > 0)
+                row_win_load<TI, DOWN>(a, t, e, w0, lane, col_off, cur);
+            int j = cur.en.x;
+            float sv = 0.f;
+            if (DOWN) {
+                float u = 0.f;
+                if (nch == 8) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                        u += cur.pv[c];
+                } else if (w0 + lane < e) {
+                    for (int c = 0; c < nch; ++c)
+                        u += a.w.p[(rbase + w0 + lane) * nch + c];
+                }
+                sv = __int_as_float(cur.en.y) * u;
+            }
+            const int n = e - w0 < 64 ? e - w0 : 64;
+            // the next row's first window, requested before this window's weight stream
+            RowWin<TI, DOWN> nxt;
+            if (PASS_PREFETCH && w0 + 64 >= e && rn < PASS_ROWS)
+                row_win_load<TI, DOWN>(a, tr(rn), er(rn), 0, lane, col_off, nxt);
+            for (int k0 = 0; k0 < n; k0 += EPI * PASS_U) {
+                u32x4 wv[PASS_U];
+                float sc[PASS_U];
+#pragma unroll
+                for (int u = 0; u < PASS_U; ++u) {
+                    const int kk = k0 + u * EPI + q;
+                    const int jj = __shfl(j, kk, 64);
+                    sc[u] = DOWN ? __shfl(sv, kk, 64) : 0.f;
+                    wv[u] = kk < n ? ldg16(wbase + (int64_t)jj * row_bytes) : u32x4{0, 0, 0, 0};
+                }
+                if (DOWN) {
+#pragma unroll
+                    for (int u = 0; u < PASS_U; ++u) {
+                        if (k0 + u * EPI + q < n) {
+#pragma unroll
+                            for (int e2 = 0; e2 < E; ++e2)
+                                acc[e2] = fmaf(sc[u], chunk_elem<TI>(wv[u], e2), acc[e2]);
+                        }
+                    }
+                } else {
+                    float part[PASS_U];
+#pragma unroll
+                    for (int u = 0; u < PASS_U; ++u) {
+                        part[u] = 0.f;
+#pragma unroll
+                        for (int e2 = 0; e2 < E; ++e2)
+                            part[u] = fmaf(xf[e2], chunk_elem<TI>(wv[u], e2), part[u]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < PASS_U; ++u)
+                        part[u] = group_sum_last<LPE>(part[u]);
+                    if (pc == LPE - 1) {
+#pragma unroll
+                        for (int u = 0; u < PASS_U; ++u) {
+                            const int kk = k0 + u * EPI + q;
+                            if (kk < n)
+                                a.w.p[(rbase + w0 + kk) * nch + csl] = part[u];
+                        }
                     }
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's list stores are done
-            __builtin_amdgcn_wave_barrier();
-            const int n = ctot - win < WLIST ? ctot - win : WLIST;
-            const int ngroups = n / G;
-            group_stream<TI, NC, G>(a, list, 0, 1, ngroups, lane, row_bytes, xf, yacc);
-            for (int e0 = ngroups * G; e0 < n; ++e0) {
-                Group<TI, NC, 1> g1;
-                group_load<TI, NC, 1>(a, list, e0, lane, row_bytes, g1);
-                group_apply<TI, NC, 1>(g1, xf, yacc);
+            if (PASS_PREFETCH && w0 + 64 >= e && rn < PASS_ROWS)
+                cur = nxt;
+        }
+        if (DOWN) {
+            // the EPI lane groups hold partial sums of the same columns: fixed butterfly
+#pragma unroll
+            for (int m = LPE; m < 64; m <<= 1)
+#pragma unroll
+                for (int e2 = 0; e2 < E; ++e2)
+                    acc[e2] += __shfl_xor(acc[e2], m, 64);
+            if (q == 0) {
+                float *yp = a.y + (int64_t)t * a.d + csl * a.cw + pc * E;
+#pragma unroll
+                for (int e4 = 0; e4 < E; e4 += 4)
+                    *reinterpret_cast<float4 *>(yp + e4) = make_float4(acc[e4], acc[e4 + 1], acc[e4 + 2], acc[e4 + 3]);
             }
-            __builtin_amdgcn_wave_barrier();  // list reads done before the next window's stores
         }
+        r = rn;
+        if (!PASS_PREFETCH && r < PASS_ROWS)
+            row_win_load<TI, DOWN>(a, tr(r), er(r), 0, lane, col_off, cur);
     }
-
-    // The NWV partial rows meet in LDS; wave w adds columns [w d/NWV, (w+1) d/NWV)
-    // as ((p0 + p1) + p2) + p3.
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int q = 0; q < E / 4; ++q)
-            *reinterpret_cast<float4 *>(&part[wave][((lane + 64 * c) * E) + 4 * q]) =
-                make_float4(yacc[c][4 * q], yacc[c][4 * q + 1], yacc[c][4 * q + 2], yacc[c][4 * q + 3]);
-    __syncthreads();
-    for (int i = tid * 4; i < a.d; i += 64 * NWV * 4) {
-        float4 acc4 = *reinterpret_cast<const float4 *>(&part[0][i]);
-#pragma unroll
-        for (int w = 1; w < NWV; ++w) {
-            const float4 p4 = *reinterpret_cast<const float4 *>(&part[w][i]);
-            acc4.x += p4.x;
-            acc4.y += p4.y;
-            acc4.z += p4.z;
-            acc4.w += p4.w;
-        }
-        *reinterpret_cast<float4 *>(yrow + i) = acc4;
-    }
+#undef tr
+#undef er
 }
 
-template <typename TI, int NC>
-static hipError_t fused_go(const FusedArgs<TI> &a, hipStream_t s)
+// Column slices: the widest cw = 64 * 2^k with at most 64 16-byte pieces per
+// row slice and d / cw >= 8 slices, else cw = 64.
+int fused_slice_cols(int d, int esz)
 {
-    if (a.T == 0)
-        return hipSuccess;
-    ffn_fused_kernel<TI, NC, FUSED_G><<<dim3(a.T), dim3(64 * NWV), 0, s>>>(a);
+    const int max_cw = esz == 2 ? 512 : 256;
+    for (int cw = max_cw; cw >= 64; cw >>= 1)
+        if (d % cw == 0 && d / cw >= 8)
+            return cw;
+    return 64;
+}
+
+FusedWs fused_ws_layout(void *base, int T, int F, int tile_w, int cap, int d, int esz)
+{
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    FusedWs w{};
+    w.nch = d / fused_slice_cols(d, esz);
+    if (T == 0)
+        return w;  // nothing to hold (bytes = 0)
+    const size_t slots = (size_t)T * (size_t)(F / tile_w) * (size_t)cap;
+    const size_t o_row = 0;
+    const size_t o_ent = o_row + up((size_t)T * 4);
+    const size_t o_p = o_ent + up(slots * sizeof(int2));
+    w.bytes = o_p + up(slots * (size_t)w.nch * sizeof(float));
+    if (base) {
+        char *b = static_cast<char *>(base);
+        w.row_e = reinterpret_cast<int32_t *>(b + o_row);
+        w.ent = reinterpret_cast<int2 *>(b + o_ent);
+        w.p = reinterpret_cast<float *>(b + o_p);
+    }
+    return w;
+}
+
+template <typename TI, int LPE>
+static hipError_t passes_go(const PassArgs<TI> &a, hipStream_t s)
+{
+    const int groups = (a.T + PASS_WAVES * PASS_ROWS - 1) / (PASS_WAVES * PASS_ROWS);
+    ffn_pass_kernel<TI, LPE, false><<<dim3(groups * a.w.nch), dim3(64 * PASS_WAVES), 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    ffn_pass_kernel<TI, LPE, true><<<dim3(groups * a.w.nch), dim3(64 * PASS_WAVES), 0, s>>>(a);
     return hipGetLastError();
 }
 
+// stage 0: the entries kernel (with row_ovf / work when given); stage 1: the
+// two passes; stage 2: both.
 template <typename TI>
-static hipError_t fused_dispatch(const int32_t *cnt, const void *val, const uint8_t *idx, const int32_t *order,
-                                 int T, int F, int tile_w, int cap, const void *x, const void *wu_t, const void *wd,
-                                 int d, float *y, hipStream_t s)
+static hipError_t fused_dispatch(int stage, const int32_t *cnt, const void *val, const uint8_t *idx,
+                                 const int32_t *order, int T, int F, int tile_w, int cap, const void *x,
+                                 const void *wu_t, const void *wd, int d, float *y, void *ws, int32_t *row_ovf,
+                                 int32_t *work, hipStream_t s)
 {
-    FusedArgs<TI> a{cnt, static_cast<const TI *>(val), idx, order, T, F / tile_w, tile_w, cap, F,
-                    static_cast<const TI *>(x), static_cast<const TI *>(wu_t), static_cast<const TI *>(wd),
-                    d, (int)((int64_t)d * Elt<TI>::SIZE / 16), y};
-    const int nch = a.nchunks;
-    if (nch <= 64)
-        return fused_go<TI, 1>(a, s);
-    if (nch <= 128)
-        return fused_go<TI, 2>(a, s);
-    if (nch <= 256)
-        return fused_go<TI, 4>(a, s);
-    return fused_go<TI, 8>(a, s);
+    if (T == 0)
+        return hipSuccess;
+    constexpr int SZ = Elt<TI>::SIZE;
+    const FusedWs w = fused_ws_layout(ws, T, F, tile_w, cap, d, SZ);
+    PassArgs<TI> a{cnt, static_cast<const TI *>(val), idx, order, T, F / tile_w, tile_w, cap, F,
+                   static_cast<const TI *>(x), static_cast<const TI *>(wu_t), static_cast<const TI *>(wd), d,
+                   w, y, d / w.nch, row_ovf, work};
+    if (stage != 1) {
+        ffn_entries_kernel<TI><<<dim3((T + PASS_WAVES - 1) / PASS_WAVES), dim3(64 * PASS_WAVES), 0, s>>>(a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess || stage == 0)
+            return e;
+    }
+    const int lpe = a.cw * SZ / 16;  // 16-byte pieces per row slice (a power of two, 8..64)
+    if (lpe == 8)
+        return passes_go<TI, 8>(a, s);
+    if (lpe == 16)
+        return passes_go<TI, 16>(a, s);
+    if (lpe == 32)
+        return passes_go<TI, 32>(a, s);
+    return passes_go<TI, 64>(a, s);
+}
+
+hipError_t launch_ffn_entries(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F,
+                              int tile_w, int cap, int d, void *ws, int32_t *row_ovf, int32_t *work, hipStream_t s)
+{
+    if (vdtype == 1)
+        return fused_dispatch<__bf16>(0, cnt, val, idx, nullptr, T, F, tile_w, cap, nullptr, nullptr, nullptr, d,
+                                      nullptr, ws, row_ovf, work, s);
+    return fused_dispatch<float>(0, cnt, val, idx, nullptr, T, F, tile_w, cap, nullptr, nullptr, nullptr, d, nullptr,
+                                 ws, row_ovf, work, s);
+}
+
+hipError_t launch_ffn_passes(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx,
+                             const int32_t *order, int T, int F, int tile_w, int cap, const void *x, const void *wu_t,
+                             const void *wd, int d, float *y, void *ws, hipStream_t s)
+{
+    if (vdtype == 1)
+        return fused_dispatch<__bf16>(1, cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, ws, nullptr,
+                                      nullptr, s);
+    return fused_dispatch<float>(1, cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, ws, nullptr, nullptr,
+                                 s);
 }
 
 hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, const int32_t *order,
                             int T, int F, int tile_w, int cap, const void *x, const void *wu_t, const void *wd, int d,
-                            float *y, hipStream_t s)
+                            float *y, void *ws, hipStream_t s)
 {
     if (vdtype == 1)
-        return fused_dispatch<__bf16>(cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, s);
-    return fused_dispatch<float>(cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, s);
+        return fused_dispatch<__bf16>(2, cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, ws, nullptr,
+                                      nullptr, s);
+    return fused_dispatch<float>(2, cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, ws, nullptr, nullptr,
+                                 s);
 }
 
 // ------------------------------------------------------------------ decode-shaped calls

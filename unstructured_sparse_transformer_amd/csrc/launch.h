@@ -51,11 +51,35 @@ hipError_t launch_dense_gate_up(int vdtype, const void *x, int T, const void *wg
 hipError_t launch_down(int vdtype, const void *p, const void *wd, const int32_t *ovf_rows, const int32_t *n_ovf,
                        int max_ovf, int F, int d, float *y, float *part, int splits, hipStream_t s);
 
-// Fused up/down from TwELL for every row (overflow rows -> 0); workgroup i
-// handles row order[i] (row i when order is null).
+// Workspace of the fused step (256-byte aligned sections).
+struct FusedWs {
+    int32_t *row_e;  // [T] stored entries of each row (0 for an overflow row)
+    int2 *ent;       // [T][n_b cap] each row's entries (neuron, gate value bits), packed first
+    float *p;        // [T][n_b cap][nch] partial dot products of u over d's column slices
+    int nch;
+    size_t bytes;
+};
+FusedWs fused_ws_layout(void *base, int T, int F, int tile_w, int cap, int d, int esz);
+
+// Width of the fused step's column slices of d for element size esz.
+int fused_slice_cols(int d, int esz);
+
+// Fused up/down from TwELL for every row (overflow rows -> 0), rows started
+// in `order` (ascending when null): the entries kernel, an up pass writing
+// each stored entry's partial dot products, a down pass writing y.
 hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, const int32_t *order,
                             int T, int F, int tile_w, int cap, const void *x, const void *wu_t, const void *wd, int d,
-                            float *y, hipStream_t s);
+                            float *y, void *ws, hipStream_t s);
+
+// The fused step in two parts, for the one-call path: the entries kernel,
+// which also writes row_ovf[t] (some tile of row t has cnt > cap) and
+// work[t] (stored entries of row t, 0 for an overflow row) as the partition's
+// flag step does; then, after the compaction, the two passes.
+hipError_t launch_ffn_entries(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F,
+                              int tile_w, int cap, int d, void *ws, int32_t *row_ovf, int32_t *work, hipStream_t s);
+hipError_t launch_ffn_passes(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx,
+                             const int32_t *order, int T, int F, int tile_w, int cap, const void *x, const void *wu_t,
+                             const void *wd, int d, float *y, void *ws, hipStream_t s);
 
 // Decode-shaped calls (T <= DEC_MAX_T, bf16): gate into w.z, TwELL, overflow
 // flags / list / count, work order, and the gather's chunking.
