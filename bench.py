@@ -58,7 +58,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="target CPU-oracle time per measurement (dense / sparse x 1 thread / all threads)")
     ap.add_argument("--no-energy", action="store_true", help="skip the energy-per-token measurement")
     ap.add_argument("--no-stats", action="store_true", help="skip the gate-statistics variant timing")
     ap.add_argument("--no-conversions", action="store_true", help="skip the hybrid <-> dense conversion timing")
@@ -142,10 +143,12 @@ def source_digest(paths):
 
 
 def measured_traffic(kernel, workload):
-    """HBM-side bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the calibration kernel's
-    known/measured ratio), or None when no summary exists for this workload or
-    the kernel's sources changed since the counters were taken."""
+    """Fabric-side (L2-miss) bytes per launch of `kernel` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the
+    calibration kernel's known/measured ratio), or None when no summary exists
+    for this workload or the kernel's sources changed since the counters were
+    taken.  These bytes go to or come from the MALL or HBM: an upper bound on
+    the kernel's HBM traffic, not HBM traffic itself."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
@@ -156,6 +159,105 @@ def measured_traffic(kernel, workload):
             c.get("sources", {}).get(kernel, [])):
         return None
     return k["fetch_bytes"] * c["calibration"]["read_factor"] + k["write_bytes"] * c["calibration"]["write_factor"]
+
+
+FUSED_KERNELS = ("row_flags_kernel", "ffn_entries_kernel", "ffn_pass_kernel_up", "ffn_pass_kernel_down")
+
+
+def pct(ms):
+    """median, p10, p90 (ms) of a list of per-launch times."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.quantile(a, 0.1)), 4),
+            "p90": round(float(np.quantile(a, 0.9)), 4), "n": int(a.size)}
+
+
+def gpu_state():
+    """GPU clock (current and maximum) and power cap from amdsmi, when available."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as ex:
+        return {"error": f"amdsmi unavailable: {ex!r}"}
+    try:
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        st = {}
+        try:
+            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            st["sclk_mhz"] = c.get("clk")
+            st["sclk_max_mhz"] = c.get("max_clk")
+        except Exception as ex:
+            st["sclk_error"] = repr(ex)
+        try:
+            pc = amdsmi.amdsmi_get_power_cap_info(h)
+            cap = pc.get("power_cap")
+            st["power_cap_w"] = round(cap / 1e6, 1) if cap and cap > 1e5 else cap
+        except Exception as ex:
+            st["power_cap_error"] = repr(ex)
+        return st
+    finally:
+        amdsmi.amdsmi_shut_down()
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle timed on this host: the scalar C library built here with
+    -O3 -march=native (no BLAS anywhere), (a) the dense FFN -- z and u as
+    scalar dot products, y = (ReLU(z) * u) . W_d -- and (b) what the path
+    computes -- the gate as scalar dot products, the TwELL packer, the
+    partition, the dense backup and the sum over the active neurons -- each
+    with one thread and with all threads, on the first rows of the workload
+    (a bounded sample sized to about `seconds` per measurement)."""
+    import tempfile
+
+    import numpy as np
+
+    import oracle
+    from oracle import build as obuild
+    lib = obuild.build(native=True, out=os.path.join(tempfile.gettempdir(), f"twell_oracle_native_{os.getpid()}.so"))
+    oracle.load(lib)
+    all_threads = oracle.max_threads()
+
+    def dense(sub):
+        r = np.arange(sub.T)
+        z = oracle.matmul_rows(sub.x, r, sub.wg_t)
+        u = oracle.matmul_rows(sub.x, r, sub.wu_t)
+        oracle.ffn_dense(z, u, sub.wd)
+
+    def sparse(sub):
+        z = oracle.matmul_rows(sub.x, np.arange(sub.T), sub.wg_t)
+        t = oracle.pack_twell(z, sub.tile_w, sub.cap, sub.dtype)
+        _, ovf_rows, _ = oracle.partition_overflow(t.cnt, sub.cap)
+        oracle.dense_backup(z, ovf_rows, sub.dtype)
+        oracle.ffn_active(z, sub.x, sub.wu_t, sub.wd, sub.dtype)
+
+    res = {}
+    for threads in (1, all_threads):
+        oracle.set_threads(threads)
+        for name, fn in (("dense", dense), ("sparse", sparse)):
+            n = min(8, wl.T)
+            t0 = time.perf_counter()
+            fn(wl.rows(0, n))
+            dt0 = time.perf_counter() - t0
+            n2 = int(min(wl.T, max(n, n * seconds / max(dt0, 1e-4))))
+            t0 = time.perf_counter()
+            fn(wl.rows(0, n2))
+            dt = time.perf_counter() - t0
+            res[(name, threads)] = (n2, dt)
+    oracle.load()
+    try:
+        os.remove(lib)
+    except OSError:
+        pass
+    tps = {k: round(n / dt, 1) for k, (n, dt) in res.items()}
+    return {"value": tps[("sparse", all_threads)], "unit": "tokens/s", "cores": all_threads, "kind": "oracle",
+            "sample": (f"first {res[('sparse', all_threads)][0]} of {wl.T} tokens of {wl.name}: scalar C oracle "
+                       f"(fp64, no BLAS) -- gate, TwELL packer, partition, dense backup, sum over active neurons "
+                       f"({res[('sparse', all_threads)][1]:.1f} s)"),
+            "dense_tokens_per_s": tps[("dense", all_threads)],
+            "one_thread": {"sparse_tokens_per_s": tps[("sparse", 1)], "dense_tokens_per_s": tps[("dense", 1)]},
+            "samples": {f"{k[0]}_{k[1]}t": {"rows": n, "s": round(dt, 2)} for k, (n, dt) in res.items()},
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "os_cpu_count": os.cpu_count(),
+            "build": obuild.build_command(native=True)}
 
 
 def main():
@@ -260,9 +362,19 @@ def main():
         step_gate_events(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    gate_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][1]) for k in range(args.steps)]))
+    gate_all = [evs[k][0].elapsed_time(evs[k][1]) for k in range(args.steps)]
+    gate_ms = float(np.mean(gate_all))
     ms_per_step = wall * 1e3 / args.steps
     value = wl.T * args.steps / wall
+
+    # ---- per-step distribution: 50 steps, each between device-scope events
+    dist_ev = [[DevEvent() for _ in range(2)] for _ in range(50)]
+    for e in dist_ev:
+        e[0].record()
+        step()
+        e[1].record()
+    torch.cuda.synchronize()
+    step_all = [e[0].elapsed_time(e[1]) for e in dist_ev]
 
     # ---- per-stage breakdown (after the timed region; events between all stages)
     sev = [[DevEvent() for _ in range(3)] for _ in range(args.steps)]
@@ -304,12 +416,18 @@ def main():
         union = int(act.sum().item())
     compulsory = union * 2 * wl.d * esz + per_token
     fused_ms = float(stage_ms[2])
-    fused = {"kernel": "ffn_fused_kernel", "ms": round(fused_ms, 4), "entries": entries,
+    fab = [measured_traffic(k, wl.name) for k in FUSED_KERNELS]
+    fused = {"kernels": "twell_ffn_fused: row_flags_kernel + ffn_entries_kernel + ffn_pass_kernel (up pass) + "
+                        "ffn_pass_kernel (down pass)",
+             "ms": round(fused_ms, 4), "entries": entries,
              "gather_bytes": gather_bytes, "compulsory_bytes": compulsory,
              "gather_GBps": round((gather_bytes + per_token) / (fused_ms * 1e-3) / 1e9, 1),
              "compulsory_GBps": round(compulsory / (fused_ms * 1e-3) / 1e9, 1),
              "compulsory_frac_hbm": round(compulsory / (fused_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-             "traffic": measured_traffic("ffn_fused_kernel", wl.name)}
+             "fabric_bytes": None if None in fab else round(sum(fab)),
+             "note": "compulsory_frac_hbm = compulsory bytes / time / 8 TB/s (the roofline fraction); "
+                     "gather_GBps counts every gathered weight row (served mostly from L2); fabric_bytes = "
+                     "calibrated FETCH_SIZE + WRITE_SIZE of the step's kernels (L2-miss traffic to MALL/HBM)"}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -320,6 +438,9 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.F, "tile_w": wl.tile_w,
                    "cap": wl.cap, "max_ovf": max_ovf, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "step_ms_dist": pct(step_all),
+        "gate_ms_dist": pct(gate_all),
+        "gpu": gpu_state(),
         "stages_ms": {"pack_gate": round(float(main_ms[0]), 4), "ffn_from_gate": round(float(main_ms[1]), 4),
                       "split_calls": {"pack_gate": round(float(stage_ms[0]), 4),
                                       "partition_overflow": round(float(stage_ms[1]), 4),
@@ -354,6 +475,31 @@ def main():
                              "pack_gate_stats_ms": round(s_ms, 4), "overhead_frac": round(s_ms / p_ms - 1, 4),
                              "dead_neurons": int((ncnt == 0).sum().item()),
                              "mean_l1_per_token": round(float(l1.sum(1).mean().item()), 4)}
+
+    # ---- the same gate GEMM with a plain dense store of ReLU(z) (twell_gate_dense)
+    # against twell_pack_gate, alternating: the price of the TwELL epilogue
+    if wl.T * wl.F * esz <= (4 << 30):
+        hd = torch.empty((wl.T, wl.F), dtype=dt, device=dev)
+        plain_ev, twell_ev = [], []
+        for k in range(args.steps):
+            for fn, acc in ((lambda: tw.twell_gate_dense(x, wg, hd), plain_ev),
+                            (lambda: tw.twell_pack_gate(x, wg, hy.ell), twell_ev)):
+                ev = [DevEvent() for _ in range(2)]
+                ev[0].record()
+                fn()
+                ev[1].record()
+                acc.append(ev)
+        torch.cuda.synchronize()
+        pd = [e[0].elapsed_time(e[1]) for e in plain_ev]
+        pt = [e[0].elapsed_time(e[1]) for e in twell_ev]
+        out["gate_plain_store"] = {
+            "kernel": "gate_dense_kernel (same GEMM core and tiles, epilogue: ReLU(z) stored densely in the "
+                      "storage type)",
+            "dense_ms": pct(pd), "twell_ms": pct(pt),
+            "twell_epilogue_ms": round(float(np.median(pt) - np.median(pd)), 4),
+            "dense_store_bytes": int(wl.T * wl.F * esz),
+            "twell_store_bytes": int(out["memory"]["twell_bytes"])}
+        del hd
 
     # ---- hybrid <-> dense conversions of this layer's activations (the training
     # kernels), HBM-bound: algorithmic bytes = the dense side (T x F elements)
@@ -493,35 +639,7 @@ def main():
 
     # ---- CPU oracle on a bounded sample of the same workload (rank 0, N=1)
     if not args.no_cpu_baseline:
-        import oracle
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-
-        def oracle_step(rows):
-            sub = wl.rows(0, rows)
-            z = oracle.gate(sub.x, sub.wg_t)
-            t = oracle.pack_twell(z, sub.tile_w, sub.cap, sub.dtype)
-            _, ovf_rows, _ = oracle.partition_overflow(t.cnt, sub.cap)
-            oracle.dense_backup(z, ovf_rows, sub.dtype)
-            oracle.ffn_active(z, sub.x, sub.wu_t, sub.wd, sub.dtype)
-
-        n = min(256, wl.T)
-        t1 = time.perf_counter()
-        oracle_step(n)
-        dt1 = time.perf_counter() - t1
-        n2 = int(min(wl.T, max(n, n * args.cpu_seconds / max(dt1, 1e-3))))
-        n2 = max(n, (n2 // 256) * 256)
-        # repeat the sample until about cpu_seconds of work have been timed
-        reps, dt2 = 0, 0.0
-        while reps == 0 or (dt2 < args.cpu_seconds and reps < 64):
-            t2 = time.perf_counter()
-            oracle_step(n2)
-            dt2 += time.perf_counter() - t2
-            reps += 1
-        out["cpu_baseline"] = {"value": round(n2 * reps / dt2, 1), "unit": "tokens/s", "cores": cores,
-                               "kind": "oracle",
-                               "sample": f"first {n2} of {wl.T} tokens of {wl.name}, {reps} time(s): fp64 numpy "
-                                         f"gate + C TwELL packer, partition, dense backup and fused sum "
-                                         f"({dt2:.1f} s)"}
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -12,6 +12,7 @@
  *   inference   twell_ffn_forward (the whole layer in one call),
  *               twell_ffn_from_gate (the layer after twell_pack_gate[_stats]),
  *               twell_pack_gate, twell_partition_overflow, twell_pack_gate_hybrid,
+ *               twell_gate_dense (the gate with a plain dense epilogue),
  *               twell_ffn_fused, twell_ffn_overflow, twell_ffn_hybrid,
  *               twell_ffn_decode (T <= 64), twell_ffn_decode_noalloc
  *   statistics  twell_pack_gate_stats
@@ -118,6 +119,20 @@ typedef struct twell_hybrid_t {
  *   h    : output TwELL; writes every element of h->cnt, h->val, h->idx.
  * Returns TWELL_OK or a negative twell_status. */
 TWELL_API int twell_pack_gate(const void *x, const void *wg_t, int32_t d, const twell_t *h, void *stream);
+
+/* The gate GEMM without the TwELL epilogue (section 2.1 of the page: the
+ * gate activation ReLU(x . W_g) that TwELL encodes, here stored densely):
+ *   h : device [T][F], vdtype, every element written with
+ *       ReLU(z) rounded to nearest even (z the fp32 accumulator; the same
+ *       values the dense backup holds), element-aligned.
+ * The same GEMM core and tiles as twell_pack_gate, with a plain store
+ * epilogue, so the difference between the two prices the TwELL packing; its
+ * output is the dense activation twell_dense_to_hybrid takes.
+ *   x : device [T][d], wg_t : device [F][d] (16-byte aligned), vdtype as
+ *   enum twell_dtype; d and F multiples of 64.
+ * Returns TWELL_OK or a negative twell_status. */
+TWELL_API int twell_gate_dense(const void *x, const void *wg_t, int32_t d, int32_t T, int32_t F, int32_t vdtype,
+                               void *h, void *stream);
 
 /* twell_pack_gate plus activation statistics taken in the same epilogue
  * (section 2.4 of the page: the L1 penalty on the activations that training

@@ -61,14 +61,34 @@ _lib = None
 VDTYPE = {"exact": -1, "f64": -1, "f32": 0, "bf16": 1}
 
 
-def _load():
+def load(path: str = None):
+    """Use the oracle library at `path` (default oracle/liboracle.so, built
+    when missing) for every later call; returns it."""
+    global _lib
+    _lib = None
+    return _load(path)
+
+
+def set_threads(n: int):
+    """Threads of the oracle's OpenMP loops (for timing; results do not depend on it)."""
+    _load().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+def _load(path: str = None):
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    path = path or _LIB_PATH
+    if not os.path.exists(path):
         from . import build as _b
         _b.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_max_threads.restype = ctypes.c_int
     P = ctypes.c_void_p
     I = ctypes.c_int
     lib.orc_round_array.argtypes = [P, ctypes.c_int64, I, P]

@@ -30,9 +30,11 @@
  *
  * Arithmetic: fp64 throughout, plain loops in the order of the definitions
  * (ascending k for dot products, ascending neuron j for the output sum).
- * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC.
+ * Build: gcc -O3 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC (no
+ * contraction or reassociation, so the flags do not change any result).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -63,6 +65,10 @@ static double orc_store(double v, int vdtype)
         f = orc_bf16_rne(f);
     return (double)f;
 }
+
+/* Threads of the OpenMP loops below (timing only; results do not depend on it). */
+EXPORT void orc_set_threads(int n) { omp_set_num_threads(n); }
+EXPORT int orc_max_threads(void) { return omp_get_max_threads(); }
 
 EXPORT void orc_round_array(const double *in, int64_t n, int vdtype, double *out)
 {

@@ -68,3 +68,18 @@ def _unbound_loads(path):
 def test_bench_and_entry_names_resolve():
     for f in ("bench.py", "__graft_entry__.py"):
         assert _unbound_loads(os.path.join(ROOT, f)) == [], f
+
+
+def test_cpu_baseline_leg_runs_on_host():
+    """bench.py's cpu_baseline leg (the natively built scalar oracle, dense and
+    sparse, one thread and all threads) on the tiny workload, host only."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from workloads import make_tiny
+    r = bench.cpu_baseline(make_tiny(), 0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["cores"] >= 1
+    assert r["value"] > 0 and r["dense_tokens_per_s"] > 0
+    assert r["one_thread"]["sparse_tokens_per_s"] > 0 and r["one_thread"]["dense_tokens_per_s"] > 0
+    assert "-march=native" in r["build"] and "-ffp-contract=off" in r["build"]
+    import oracle
+    assert oracle.max_threads() >= 1  # the portable library is back in use

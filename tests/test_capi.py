@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert set(names) == set(tw.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.twell_version() == 200
+    assert lib.twell_version() == 201
 
 
 def test_status_strings():
@@ -85,9 +85,9 @@ def test_fused_and_hybrid_validation():
     d = _desc()
     need_f = lib.twell_workspace_bytes(16, 512, 128, 8, 0, 64, 1)
     slots = 16 * 4 * 8                                                    # T * n_b * cap
-    # row entry counts (256 B here), each row's packed entries (neuron, gate value: 8 B per slot) and
-    # (d / 64) partial dot products per slot
-    assert need_f == 256 + slots * 8 + slots * 1 * 4
+    # row entry counts by row and in work order (256 B each here), each row's packed entries (neuron,
+    # gate value: 8 B per slot) and (d / 64) partial dot products per slot
+    assert need_f == 2 * 256 + slots * 8 + slots * 1 * 4
     f = lib.twell_ffn_fused
     r = ctypes.byref(d)
     assert f(r, None, GOOD, GOOD, GOOD, 64, None, GOOD, need_f, None) == -1       # y NULL
@@ -278,3 +278,18 @@ def test_ffn_backward_validation():
     big = dict(T=1 << 19, F=16384, w=32, cap=7)
     assert call(hy(max_ovf=1 << 14, **big), d=2048, ws_bytes=0) == -3
     assert call(hy(max_ovf=(1 << 14) - 1, **big), d=2048, ws_bytes=0) == -6   # one row less: next check
+
+
+def test_gate_dense_validation():
+    lib = tw.load()
+    f = lib.twell_gate_dense
+    assert f(GOOD, GOOD, 64, 16, 512, 2, GOOD, None) == -4         # dtype
+    assert f(GOOD, GOOD, 60, 16, 512, 1, GOOD, None) == -3         # d % 64
+    assert f(GOOD, GOOD, 64, 16, 500, 1, GOOD, None) == -3         # F % 64
+    assert f(GOOD, GOOD, 64, -1, 512, 1, GOOD, None) == -3
+    assert f(None, GOOD, 64, 16, 512, 1, GOOD, None) == -1         # x NULL
+    assert f(GOOD, GOOD + 8, 64, 16, 512, 1, GOOD, None) == -2     # W_g misaligned
+    assert f(GOOD, GOOD, 64, 16, 512, 1, None, None) == -1         # h NULL
+    assert f(GOOD, GOOD, 64, 16, 512, 1, GOOD + 1, None) == -2     # h not element-aligned
+    assert f(GOOD, GOOD, 2048, 1 << 20, 512, 1, GOOD, None) == -3  # x = 4 GiB
+    assert f(None, None, 64, 0, 512, 1, None, None) == 0           # T = 0

@@ -6,7 +6,7 @@ memory and the current HIP stream.  There is no CPU fallback: ``load()``
 raises when the library is missing, and every call raises on a non-OK status.
 
 The functions carry the C names (``include/twell.h``):
-``twell_ffn_forward``, ``twell_ffn_from_gate``, ``twell_pack_gate``, ``twell_pack_gate_stats``, ``twell_partition_overflow``,
+``twell_ffn_forward``, ``twell_ffn_from_gate``, ``twell_pack_gate``, ``twell_gate_dense``, ``twell_pack_gate_stats``, ``twell_partition_overflow``,
 ``twell_pack_gate_hybrid``,
 ``twell_ffn_fused``, ``twell_ffn_overflow``, ``twell_ffn_hybrid``,
 ``twell_workspace_bytes``, ``twell_ffn_decode``,
@@ -42,7 +42,7 @@ LIB_PATH = os.path.join(_HERE, "libtwell.so")
 TWELL_F32, TWELL_BF16 = 0, 1
 STATUS = {0: "TWELL_OK", -1: "TWELL_E_NULL", -2: "TWELL_E_ALIGN", -3: "TWELL_E_SHAPE",
           -4: "TWELL_E_UNSUPPORTED", -5: "TWELL_E_HIP", -6: "TWELL_E_WORKSPACE", -7: "TWELL_E_SCRATCH"}
-EXPORTS = ("twell_ffn_forward", "twell_ffn_from_gate", "twell_pack_gate", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
+EXPORTS = ("twell_ffn_forward", "twell_ffn_from_gate", "twell_pack_gate", "twell_gate_dense", "twell_pack_gate_stats", "twell_partition_overflow", "twell_pack_gate_hybrid",
            "twell_ffn_fused", "twell_workspace_bytes", "twell_ffn_overflow", "twell_ffn_hybrid",
            "twell_ffn_decode_workspace_bytes", "twell_ffn_decode", "twell_ffn_decode_noalloc", "twell_dense_to_hybrid", "twell_hybrid_to_dense",
            "twell_compact_min_bytes", "twell_compact_hybrid", "twell_compact_to_dense",
@@ -83,6 +83,7 @@ def load(path: str = LIB_PATH):
     P, I32 = ctypes.c_void_p, ctypes.c_int32
     lib.twell_pack_gate.argtypes = [P, P, I32, ctypes.POINTER(TwellT), P]
     lib.twell_pack_gate_stats.argtypes = [P, P, I32, ctypes.POINTER(TwellT), P, P, P]
+    lib.twell_gate_dense.argtypes = [P, P, I32, I32, I32, I32, P, P]
     lib.twell_partition_overflow.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
     lib.twell_pack_gate_hybrid.argtypes = [P, P, I32, ctypes.POINTER(TwellHybridT), P]
     lib.twell_ffn_fused.argtypes = [ctypes.POINTER(TwellT), P, P, P, P, I32, P, P, ctypes.c_size_t, P]
@@ -109,7 +110,7 @@ def load(path: str = LIB_PATH):
     lib.twell_status_str.argtypes = [ctypes.c_int]
     lib.twell_status_str.restype = ctypes.c_char_p
     lib.twell_version.restype = ctypes.c_int
-    for fn in (lib.twell_pack_gate, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
+    for fn in (lib.twell_pack_gate, lib.twell_gate_dense, lib.twell_pack_gate_stats, lib.twell_partition_overflow, lib.twell_pack_gate_hybrid,
                lib.twell_ffn_fused, lib.twell_ffn_hybrid, lib.twell_ffn_overflow, lib.twell_ffn_forward,
                lib.twell_ffn_from_gate, lib.twell_ffn_decode, lib.twell_ffn_decode_noalloc,
                lib.twell_dense_to_hybrid, lib.twell_hybrid_to_dense, lib.twell_compact_hybrid,
@@ -206,6 +207,13 @@ def twell_pack_gate(x, wg_t, tw: TwELL, stream=None):
     lib = load()
     d = ctypes.byref(tw.desc())
     _check("twell_pack_gate", lib.twell_pack_gate(_ptr(x), _ptr(wg_t), int(x.shape[1]), d, _stream(stream)))
+
+
+def twell_gate_dense(x, wg_t, h, stream=None):
+    """h [T][F] (x's dtype) = ReLU(x W_g), the gate with a plain dense store."""
+    _check("twell_gate_dense", load().twell_gate_dense(_ptr(x), _ptr(wg_t), int(x.shape[1]), int(x.shape[0]),
+                                                       int(wg_t.shape[0]), vdtype_of(x.dtype), _ptr(h),
+                                                       _stream(stream)))
 
 
 def twell_pack_gate_stats(x, wg_t, tw: TwELL, neuron_cnt, l1, stream=None):

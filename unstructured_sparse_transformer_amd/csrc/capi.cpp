@@ -156,10 +156,12 @@ int launch_from_gate(const void *x, const void *wg_t, const void *wu_t, const vo
     char *ws = static_cast<char *>(workspace);
     TWELL_TRY(hip_status(twell::launch_ffn_entries(h->vdtype, h->cnt, h->val, h->idx, h->T, h->F, h->tile_w, h->cap,
                                                    d, ws + w.s_off, hy->row_ovf, hy->order, s)));
-    TWELL_TRY(hip_status(
-        twell::launch_compact_rows(hy->row_ovf, h->T, hy->max_ovf, hy->ovf_rows, hy->n_ovf, hy->order, s)));
+    const twell::FusedWs fw = twell::fused_ws_layout(ws + w.s_off, h->T, h->F, h->tile_w, h->cap, d,
+                                                     elem_size(h->vdtype));
+    TWELL_TRY(hip_status(twell::launch_compact_rows(hy->row_ovf, h->T, hy->max_ovf, hy->ovf_rows, hy->n_ovf,
+                                                    hy->order, s, fw.order_e)));
     TWELL_TRY(hip_status(twell::launch_ffn_passes(h->vdtype, h->cnt, h->val, h->idx, hy->order, h->T, h->F,
-                                                  h->tile_w, h->cap, x, wu_t, wd, d, y, ws + w.s_off, s)));
+                                                  h->tile_w, h->cap, x, wu_t, wd, d, y, ws + w.s_off, true, s)));
     if (hy->max_ovf == 0)
         return TWELL_OK;
     void *pbuf = ws + w.p_off;
@@ -209,7 +211,7 @@ int launch_decode(const void *x, const void *wg_t, const void *wu_t, const void 
 
 extern "C" {
 
-int twell_version(void) { return 200; }
+int twell_version(void) { return 201; }
 
 const char *twell_status_str(int status)
 {
@@ -245,6 +247,27 @@ int twell_pack_gate(const void *x, const void *wg_t, int32_t d, const twell_t *h
     TWELL_TRY(check_ptrs(h));
     return hip_status(twell::launch_gate_twell(h->vdtype, x, wg_t, h->T, d, h->F, h->tile_w, h->cap, h->val, h->idx,
                                                h->cnt, static_cast<hipStream_t>(stream)));
+}
+
+int twell_gate_dense(const void *x, const void *wg_t, int32_t d, int32_t T, int32_t F, int32_t vdtype, void *h,
+                     void *stream)
+{
+    if (vdtype != TWELL_F32 && vdtype != TWELL_BF16)
+        return TWELL_E_UNSUPPORTED;
+    if (T < 0 || F <= 0 || F % 64 != 0 || d <= 0 || d % 64 != 0)
+        return TWELL_E_SHAPE;
+    const int64_t lim = (int64_t)1 << 32;
+    if ((int64_t)T * d * elem_size(vdtype) >= lim || (int64_t)F * d * elem_size(vdtype) >= lim)
+        return TWELL_E_SHAPE;
+    if (T == 0)
+        return TWELL_OK;
+    TWELL_TRY(check_mat(x));
+    TWELL_TRY(check_mat(wg_t));
+    if (!h)
+        return TWELL_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(h) & (elem_size(vdtype) - 1)) != 0)
+        return TWELL_E_ALIGN;
+    return hip_status(twell::launch_gate_dense(vdtype, x, wg_t, T, d, F, h, static_cast<hipStream_t>(stream)));
 }
 
 int twell_pack_gate_stats(const void *x, const void *wg_t, int32_t d, const twell_t *h, int32_t *neuron_cnt,

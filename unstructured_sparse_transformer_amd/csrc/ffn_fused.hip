@@ -146,18 +146,23 @@ __device__ __forceinline__ void group_stream(const FusedArgs<TI> &a, const int2 
 // column slices at the usual widths), and workgroups are handed to the 8 XCDs
 // round-robin (workgroup g runs on XCD g % 8), so XCD c only ever reads
 // column slice c of x, W_u^T and W_d: the live rows' slices of one weight
-// matrix (3.4 MB at the 2B shape) stay in its 4 MB L2.  A row slice is LPE
-// 16-byte pieces; a wave serves 64 / LPE rows (consecutive work positions),
-// one per group of LPE lanes, each lane one piece, and the groups step through
-// their rows' entries together.  The up pass keeps the lane's piece of x[t] in
-// registers and writes, per entry, the partial dot product of x[t] and
-// W_u^T[j] over the slice (DPP reduction over the group's lanes) to
-// p[slot][c] (fp32).  The down pass forms s = h * (p[slot][0] + ... +
-// p[slot][nch - 1]) (fixed order) and accumulates y[t][slice] += s * W_d[j]
-// in the lanes' registers, in ascending entry order.  Every value comes from
-// one lane group in a fixed order, so the result does not depend on timing.
-// Overflow rows, and rows without entries, get y = 0 (the dense path writes
-// the overflow rows afterwards).
+// matrix (3.4 MB at the 2B shape) stay in its 4 MB L2.  A wave takes
+// PASS_ROWS rows at work positions strided across the work order (w, w + W,
+// ...: the heaviest rows, which lead the order, land in different waves),
+// learns their entry counts in one round of loads, skips the empty ones and
+// runs the others in turn, requesting the next row's entries before the
+// current row's weight stream.  A row slice is LPE 16-byte pieces: the lanes
+// take 64 / LPE entries per step, LPE lanes per entry and one piece per lane.
+// The up pass keeps the lane's piece of x[t] in registers and writes, per
+// entry, the partial dot product of x[t] and W_u^T[j] over the slice (DPP
+// reduction over the entry's lanes) to p[c][slot] (fp32; slice-major, so one
+// XCD's writes for consecutive entries share cache lines).  The down pass
+// forms s = h * (p[0][slot] + ... + p[nch - 1][slot]) (fixed order) and
+// accumulates y[t][slice] += s * W_d[j] in the lanes' registers, each lane its
+// entries in ascending order, the lane groups then added by a fixed
+// butterfly.  Every value comes from one wave in a fixed order, so the result
+// does not depend on timing.  Overflow rows, and rows without entries, get
+// y = 0 (the dense path writes the overflow rows afterwards).
 template <typename TI> struct PassArgs {
     const int32_t *cnt;
     const TI *val;
@@ -170,11 +175,12 @@ template <typename TI> struct PassArgs {
     float *y;
     int cw;                   // width of a column slice (d = w.nch * cw)
     int32_t *row_ovf, *work;  // optional (one-call path): overflow flag, work value
+    const int32_t *order_e;   // optional: entry counts in work order (else row_e[order[i]])
 };
 
 constexpr int PASS_WAVES = 4;
 #ifndef PASS_STEPS
-#define PASS_STEPS 4
+#define PASS_STEPS 8
 #endif
 #ifndef PASS_PREFETCH
 #define PASS_PREFETCH 1
@@ -279,10 +285,9 @@ __device__ __forceinline__ void row_win_load(const PassArgs<TI> &a, int t, int e
     r.en = ok ? a.w.ent[rbase + k] : make_int2(0, 0);
     if (DOWN) {
         if (a.w.nch == 8) {
-            const float4 q0 = ok ? *reinterpret_cast<const float4 *>(a.w.p + (rbase + k) * 8) : make_float4(0, 0, 0, 0);
-            const float4 q1 = ok ? *reinterpret_cast<const float4 *>(a.w.p + (rbase + k) * 8 + 4) : make_float4(0, 0, 0, 0);
-            r.pv[0] = q0.x; r.pv[1] = q0.y; r.pv[2] = q0.z; r.pv[3] = q0.w;
-            r.pv[4] = q1.x; r.pv[5] = q1.y; r.pv[6] = q1.z; r.pv[7] = q1.w;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                r.pv[c] = ok ? a.w.p[c * a.w.pstride + rbase + k] : 0.f;
         }
     } else if (w0 == 0) {
         r.xv = ldg16((const char *)a.x + (int64_t)t * a.d * Elt<TI>::SIZE + col_off);
@@ -314,9 +319,11 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
     int tv = -1, ev = 0;
     if (lane < PASS_ROWS && ip < a.T) {
         tv = a.order ? a.order[ip] : ip;
+        if (a.order_e)
+            ev = a.order_e[ip];  // the same round of loads as the row
         tv = (unsigned)tv < (unsigned)a.T ? tv : -1;  // not a permutation: not ours to write
     }
-    if (tv >= 0)
+    if (tv >= 0 && !a.order_e)
         ev = a.w.row_e[tv];
     // row r of the wave: tr(r), er(r) (scalar reads of lane r)
 #define tr(r) __builtin_amdgcn_readlane(tv, (r))
@@ -375,7 +382,7 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
                         u += cur.pv[c];
                 } else if (w0 + lane < e) {
                     for (int c = 0; c < nch; ++c)
-                        u += a.w.p[(rbase + w0 + lane) * nch + c];
+                        u += a.w.p[c * a.w.pstride + rbase + w0 + lane];
                 }
                 sv = __int_as_float(cur.en.y) * u;
             }
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
                         for (int u = 0; u < PASS_U; ++u) {
                             const int kk = k0 + u * EPI + q;
                             if (kk < n)
-                                a.w.p[(rbase + w0 + kk) * nch + csl] = part[u];
+                                a.w.p[csl * a.w.pstride + rbase + w0 + kk] = part[u];
                         }
                     }
                 }
@@ -470,12 +477,15 @@ FusedWs fused_ws_layout(void *base, int T, int F, int tile_w, int cap, int d, in
         return w;  // nothing to hold (bytes = 0)
     const size_t slots = (size_t)T * (size_t)(F / tile_w) * (size_t)cap;
     const size_t o_row = 0;
-    const size_t o_ent = o_row + up((size_t)T * 4);
+    const size_t o_ord = o_row + up((size_t)T * 4);
+    const size_t o_ent = o_ord + up((size_t)T * 4);
     const size_t o_p = o_ent + up(slots * sizeof(int2));
     w.bytes = o_p + up(slots * (size_t)w.nch * sizeof(float));
+    w.pstride = (int64_t)slots;
     if (base) {
         char *b = static_cast<char *>(base);
         w.row_e = reinterpret_cast<int32_t *>(b + o_row);
+        w.order_e = reinterpret_cast<int32_t *>(b + o_ord);
         w.ent = reinterpret_cast<int2 *>(b + o_ent);
         w.p = reinterpret_cast<float *>(b + o_p);
     }
@@ -500,7 +510,7 @@ template <typename TI>
 static hipError_t fused_dispatch(int stage, const int32_t *cnt, const void *val, const uint8_t *idx,
                                  const int32_t *order, int T, int F, int tile_w, int cap, const void *x,
                                  const void *wu_t, const void *wd, int d, float *y, void *ws, int32_t *row_ovf,
-                                 int32_t *work, hipStream_t s)
+                                 int32_t *work, bool use_order_e, hipStream_t s)
 {
     if (T == 0)
         return hipSuccess;
@@ -508,7 +518,7 @@ static hipError_t fused_dispatch(int stage, const int32_t *cnt, const void *val,
     const FusedWs w = fused_ws_layout(ws, T, F, tile_w, cap, d, SZ);
     PassArgs<TI> a{cnt, static_cast<const TI *>(val), idx, order, T, F / tile_w, tile_w, cap, F,
                    static_cast<const TI *>(x), static_cast<const TI *>(wu_t), static_cast<const TI *>(wd), d,
-                   w, y, d / w.nch, row_ovf, work};
+                   w, y, d / w.nch, row_ovf, work, use_order_e ? w.order_e : nullptr};
     if (stage != 1) {
         ffn_entries_kernel<TI><<<dim3((T + PASS_WAVES - 1) / PASS_WAVES), dim3(64 * PASS_WAVES), 0, s>>>(a);
         const hipError_t e = hipGetLastError();
@@ -530,20 +540,20 @@ hipError_t launch_ffn_entries(int vdtype, const int32_t *cnt, const void *val, c
 {
     if (vdtype == 1)
         return fused_dispatch<__bf16>(0, cnt, val, idx, nullptr, T, F, tile_w, cap, nullptr, nullptr, nullptr, d,
-                                      nullptr, ws, row_ovf, work, s);
+                                      nullptr, ws, row_ovf, work, false, s);
     return fused_dispatch<float>(0, cnt, val, idx, nullptr, T, F, tile_w, cap, nullptr, nullptr, nullptr, d, nullptr,
-                                 ws, row_ovf, work, s);
+                                 ws, row_ovf, work, false, s);
 }
 
 hipError_t launch_ffn_passes(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx,
                              const int32_t *order, int T, int F, int tile_w, int cap, const void *x, const void *wu_t,
-                             const void *wd, int d, float *y, void *ws, hipStream_t s)
+                             const void *wd, int d, float *y, void *ws, bool use_order_e, hipStream_t s)
 {
     if (vdtype == 1)
         return fused_dispatch<__bf16>(1, cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, ws, nullptr,
-                                      nullptr, s);
+                                      nullptr, use_order_e, s);
     return fused_dispatch<float>(1, cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, ws, nullptr, nullptr,
-                                 s);
+                                 use_order_e, s);
 }
 
 hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, const int32_t *order,
@@ -552,9 +562,9 @@ hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, con
 {
     if (vdtype == 1)
         return fused_dispatch<__bf16>(2, cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, ws, nullptr,
-                                      nullptr, s);
+                                      nullptr, false, s);
     return fused_dispatch<float>(2, cnt, val, idx, order, T, F, tile_w, cap, x, wu_t, wd, d, y, ws, nullptr, nullptr,
-                                 s);
+                                 false, s);
 }
 
 // ------------------------------------------------------------------ decode-shaped calls

@@ -642,6 +642,70 @@ gate_twell_kernel(GemmArgs p, TwellOut<TI> o, GateStats st)
         twell_epilogue<TI, BM, BN, WM, WN, TW, Core::LDS_BYTES>(acc, smem, m0, n0, p.M, p.N, o);
 }
 
+// The same GEMM with a plain epilogue: h = ReLU(z) stored densely ([M][N],
+// the storage type, round to nearest even), straight from the accumulators
+// (a lane's 16 values of a 32 x 32 block are 16 rows of one column; the 32
+// lanes of a half-wave write 64 or 128 contiguous bytes of each row).
+template <typename TI, int BM, int BN, int WM, int WN, int KB, int STAGES, int WPE>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
+gate_dense_kernel(GemmArgs p, TI *h)
+{
+    using Core = GemmCore<TI, BM, BN, WM, WN, false, KB, STAGES>;
+    __shared__ __attribute__((aligned(16))) char smem[Core::LDS_BYTES];
+    int mt, nt;
+    tile_coords(blockIdx.x, p.MT, p.NT, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BN;
+    Core core;
+    f32x16 acc[Core::FM][Core::FN];
+    core.run(p, smem, m0, n0, p.M, p.k_begin, p.k_len, threadIdx.x, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / Core::NWN, wn = wave % Core::NWN;
+#pragma unroll
+    for (int fm = 0; fm < Core::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Core::FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + wm * WM + fm * 32 + acc_row(i, lane);
+                const int n = n0 + wn * WN + fn * 32 + (lane & 31);
+                if (m < p.M && n < p.N) {
+                    const float v = acc[fm][fn][i];
+                    store_elem(h + (int64_t)m * p.N + n, v > 0.f ? v : 0.f);
+                }
+            }
+}
+
+template <typename TI, int BM, int BN, int WM, int WN, int KB, int STAGES, int WPE>
+static hipError_t gate_dense_go(const void *x, const void *wg_t, int T, int d, int F, void *h, hipStream_t s)
+{
+    GemmArgs p{};
+    p.A = x;
+    p.lda = d;
+    p.M = T;
+    p.B = wg_t;
+    p.ldb = d;
+    p.N = F;
+    p.k_begin = 0;
+    p.k_len = d;
+    p.MT = (T + BM - 1) / BM;
+    p.NT = (F + BN - 1) / BN;
+    p.a_bytes = (uint32_t)((int64_t)T * d * sizeof(TI));
+    p.b_bytes = (uint32_t)((int64_t)F * d * sizeof(TI));
+    constexpr int NTHR = (BM / WM) * (BN / WN) * 64;
+    gate_dense_kernel<TI, BM, BN, WM, WN, KB, STAGES, WPE>
+        <<<dim3(p.MT * p.NT), dim3(NTHR), 0, s>>>(p, static_cast<TI *>(h));
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_dense(int vdtype, const void *x, const void *wg_t, int T, int d, int F, void *h,
+                             hipStream_t s)
+{
+    if (vdtype == 1)
+        return gate_dense_go<__bf16, GATE_BM, 256, GATE_WM, 128, GATE_KB, GATE_STAGES, GATE_WPE>(x, wg_t, T, d, F,
+                                                                                                 h, s);
+    return gate_dense_go<float, 64, 256, 32, 128, 128, 2, 1>(x, wg_t, T, d, F, h, s);
+}
+
 template <typename TI, int BM, int BN, int WM, int WN, int KB, int STAGES, int WPE, bool STATS>
 static hipError_t gate_twell_go(const void *x, const void *wg_t, int T, int d, int F, int tile_w, int cap, void *val,
                                 uint8_t *idx, int32_t *cnt, const GateStats &st, hipStream_t s)

@@ -66,13 +66,16 @@ __device__ __forceinline__ int work_class(int e)
 // staged in LDS and written out coalesced.  `order` holds the rows' work
 // values on entry; each chunk reads all of its values before the first
 // barrier and writes only its own positions after it.  n_ovf is the true
-// number of flagged rows.
+// number of flagged rows.  WE: also order_e[i] = the work value of the row at
+// work position i (staged in LDS beside the order), so that the fused step
+// learns a row and its entry count in one load.
 constexpr int CR_THREADS = 1024, CR_NC = 8, CR_CHUNK = 16384;  // rows per work-order chunk
 
-template <bool VEC, int ROWS>
+template <bool VEC, int ROWS, bool WE>
 __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t *__restrict__ row_ovf, int T,
                                                                   int max_ovf, int32_t *__restrict__ ovf_rows,
-                                                                  int32_t *__restrict__ n_ovf, int32_t *order)
+                                                                  int32_t *__restrict__ n_ovf, int32_t *order,
+                                                                  int32_t *__restrict__ order_e)
 {
     constexpr int NV = CR_NC + 1;  // scanned values: classes 0..7, flagged rows
     constexpr int NW = CR_THREADS / 64;
@@ -81,6 +84,7 @@ __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t 
     __shared__ int wave_tot[NW][NV];
     __shared__ int wave_off[NW + 1][NV];  // exclusive prefix over waves; row NW = totals
     __shared__ int sord[PASS];        // the chunk's work order
+    __shared__ int swork[WE ? PASS : 1];  // the work values in that order
     const int tid = threadIdx.x, wave = tid >> 6;
     int base = 0;
     for (int t0 = 0; t0 < T; t0 += PASS) {
@@ -173,6 +177,8 @@ __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t 
                 for (int q = 0; q < CR_NC; ++q)
                     p = c == q ? cpos[q] : p;
                 sord[p + (int)((used >> (8 * c)) & 0xFFu)] = t0 + i0 + k;
+                if (WE)
+                    swork[p + (int)((used >> (8 * c)) & 0xFFu)] = wk[k];
                 used += 1ull << (8 * c);
             }
         }
@@ -180,8 +186,11 @@ __global__ __launch_bounds__(CR_THREADS) void compact_rows_kernel(const int32_t 
 #pragma unroll 4
         for (int k = 0; k < ROWS; ++k) {
             const int i = k * CR_THREADS + tid;
-            if (i < nrows)
+            if (i < nrows) {
                 order[t0 + i] = sord[i];
+                if (WE)
+                    order_e[t0 + i] = swork[i];
+            }
         }
         base += tot[CR_NC];
         __syncthreads();
@@ -201,19 +210,30 @@ hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t
     return hipGetLastError();
 }
 
+template <bool WE>
+static void compact_rows_go(bool vec, bool one_pass8, const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows,
+                            int32_t *n_ovf, int32_t *order, int32_t *order_e, hipStream_t s)
+{
+    const dim3 g(1), b(CR_THREADS);
+    if (vec && one_pass8)
+        compact_rows_kernel<true, 8, WE><<<g, b, 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order, order_e);
+    else if (vec)
+        compact_rows_kernel<true, 16, WE><<<g, b, 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order, order_e);
+    else if (one_pass8)
+        compact_rows_kernel<false, 8, WE><<<g, b, 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order, order_e);
+    else
+        compact_rows_kernel<false, 16, WE><<<g, b, 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order, order_e);
+}
+
 hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows, int32_t *n_ovf,
-                               int32_t *order, hipStream_t s)
+                               int32_t *order, hipStream_t s, int32_t *order_e)
 {
     const bool vec = ((reinterpret_cast<uintptr_t>(row_ovf) | reinterpret_cast<uintptr_t>(order)) & 15u) == 0;
     const bool one_pass8 = T <= CR_THREADS * 8;  // ROWS = 8 only where its single pass is the single chunk
-    if (vec && one_pass8)
-        compact_rows_kernel<true, 8><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
-    else if (vec)
-        compact_rows_kernel<true, 16><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
-    else if (one_pass8)
-        compact_rows_kernel<false, 8><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
+    if (order_e)
+        compact_rows_go<true>(vec, one_pass8, row_ovf, T, max_ovf, ovf_rows, n_ovf, order, order_e, s);
     else
-        compact_rows_kernel<false, 16><<<dim3(1), dim3(CR_THREADS), 0, s>>>(row_ovf, T, max_ovf, ovf_rows, n_ovf, order);
+        compact_rows_go<false>(vec, one_pass8, row_ovf, T, max_ovf, ovf_rows, n_ovf, order, nullptr, s);
     return hipGetLastError();
 }
 
@@ -260,7 +280,16 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define DN_BN 128
 #endif
 #ifndef DN_MAX_SPLITS
-#define DN_MAX_SPLITS 8
+#define DN_MAX_SPLITS 16
+#endif
+#ifndef DN_TARGET_WGS
+#define DN_TARGET_WGS 256
+#endif
+#ifndef DN_ROWS_HINT
+#define DN_ROWS_HINT 256
+#endif
+#ifndef DN_PART_MB
+#define DN_PART_MB 256
 #endif
 #ifndef DU_BM
 #define DU_BM 64
@@ -453,12 +482,19 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 // transposing LDS reads, 48 KiB; fp32: transposed in LDS, 64 KiB), split
 // over K, three workgroups per CU where they fit.
 constexpr int HB_BM = 64, HB_WM = 32;
-constexpr int DN_BM = 64, DN_WM = 32;
+#ifndef DN_BM
+#define DN_BM 64
+#endif
+#ifndef DN_WM
+#define DN_WM 32
+#endif
 // Dual gate / up GEMM: 64 rows x 64 output columns per workgroup (a 128-row
 // B tile of 32-row W_g / W_u blocks), 4 waves of 32 x 64, 3-deep ring of
 // 24 KiB stages (72 KiB), two workgroups per CU (64-row blocks, 128 columns
 // and one 120 KiB workgroup per CU measured 2.5-12 us slower per call).
-constexpr int DU_WM = 32;
+#ifndef DU_WM
+#define DU_WM 32
+#endif
 
 // Workgroups for a tile loop: one per CU, at most `tiles`, rounded down to a
 // multiple of 8 when that many (keeps N columns on one XCD).
@@ -557,12 +593,16 @@ hipError_t launch_dense_gate_up(int vdtype, const void *x, int T, const void *wg
 
 int down_splits(int max_ovf, int F, int d)
 {
-    // Overflow rows are typically a few percent of max_ovf's worth of M tiles;
-    // aim for >= ~2048 workgroups over the full M range so that the active
-    // ones cover the chip.  K slices stay whole multiples of 64 elements.
-    const long tiles = (long)((max_ovf + DN_BM - 1) / DN_BM) * ((d + DN_BN - 1) / DN_BN);
+    // The rows in use (n_ovf) are known only on the device; size the split for
+    // about DN_ROWS_HINT of them (a few hundred overflow rows is the usual
+    // case), enough (tile, split) pairs for every CU, K slices whole multiples
+    // of 64, and the partial slabs ([splits][max_ovf][d] fp32) at most
+    // DN_PART_MB of workspace.
+    const long tiles = (long)((DN_ROWS_HINT + DN_BM - 1) / DN_BM) * ((d + DN_BN - 1) / DN_BN);
+    const long slab = (long)max_ovf * d * 4;
     int s = 1;
-    while (s < DN_MAX_SPLITS && tiles * s < 2048 && F % (s * 2 * 64) == 0)
+    while (s < DN_MAX_SPLITS && tiles * s < DN_TARGET_WGS && F % (s * 2 * 64) == 0 &&
+           slab * s * 2 <= ((long)DN_PART_MB << 20))
         s *= 2;
     return s;
 }

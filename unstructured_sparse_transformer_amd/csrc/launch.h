@@ -20,6 +20,11 @@ hipError_t launch_gate_twell_stats(int vdtype, const void *x, const void *wg_t, 
                                    int cap, void *val, uint8_t *idx, int32_t *cnt, int32_t *neuron_cnt, float *l1,
                                    hipStream_t s);
 
+// The gate GEMM with a plain epilogue: h [T][F] = ReLU(x . W_g) stored
+// densely in the element type.
+hipError_t launch_gate_dense(int vdtype, const void *x, const void *wg_t, int T, int d, int F, void *h,
+                             hipStream_t s);
+
 // row_ovf[t] = any tile of row t has cnt > cap; work[t] = stored entries of
 // row t (0 for an overflow row).
 hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t *row_ovf, int32_t *work,
@@ -27,8 +32,9 @@ hipError_t launch_row_flags(const int32_t *cnt, int T, int n_b, int cap, int32_t
 
 // Ascending list of flagged rows (first max_ovf of them) and their total
 // count; `order` holds the work values on entry and the work order on return.
+// With order_e: also the work value of the row at each work position.
 hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32_t *ovf_rows, int32_t *n_ovf,
-                               int32_t *order, hipStream_t s);
+                               int32_t *order, hipStream_t s, int32_t *order_e = nullptr);
 
 // dense[i][:] = ReLU(x[ovf_rows[i]] . W_g) for i < min(*n_ovf, max_ovf).
 hipError_t launch_dense_gate(int vdtype, const void *x, int T, const void *wg_t, const int32_t *ovf_rows,
@@ -53,9 +59,11 @@ hipError_t launch_down(int vdtype, const void *p, const void *wd, const int32_t 
 
 // Workspace of the fused step (256-byte aligned sections).
 struct FusedWs {
-    int32_t *row_e;  // [T] stored entries of each row (0 for an overflow row)
+    int32_t *row_e;    // [T] stored entries of each row (0 for an overflow row)
+    int32_t *order_e;  // [T] the same in work order (one-call path: written by the compaction)
     int2 *ent;       // [T][n_b cap] each row's entries (neuron, gate value bits), packed first
-    float *p;        // [T][n_b cap][nch] partial dot products of u over d's column slices
+    float *p;        // [nch][T n_b cap] partial dot products of u over d's column slices
+    int64_t pstride; // T n_b cap: distance between two column slices' partials
     int nch;
     size_t bytes;
 };
@@ -77,9 +85,10 @@ hipError_t launch_ffn_fused(int vdtype, const int32_t *cnt, const void *val, con
 // flag step does; then, after the compaction, the two passes.
 hipError_t launch_ffn_entries(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx, int T, int F,
                               int tile_w, int cap, int d, void *ws, int32_t *row_ovf, int32_t *work, hipStream_t s);
+// use_order_e: the compaction wrote the entry counts in work order (FusedWs order_e).
 hipError_t launch_ffn_passes(int vdtype, const int32_t *cnt, const void *val, const uint8_t *idx,
                              const int32_t *order, int T, int F, int tile_w, int cap, const void *x, const void *wu_t,
-                             const void *wd, int d, float *y, void *ws, hipStream_t s);
+                             const void *wd, int d, float *y, void *ws, bool use_order_e, hipStream_t s);
 
 // Decode-shaped calls (T <= DEC_MAX_T, bf16): gate into w.z, TwELL, overflow
 // flags / list / count, work order, and the gather's chunking.
