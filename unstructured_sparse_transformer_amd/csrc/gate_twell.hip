@@ -21,8 +21,11 @@
 // bf16 workgroup tile: GATE_BM x 256 with waves of GATE_WM x 128 and
 // GATE_WPE waves per SIMD.  Default: 256 x 256 with 8 waves of 64 x 128 (two
 // per SIMD, so one wave's LDS reads and barrier waits overlap the other's
-// MFMAs) fed by a 2-deep ring of 128-byte K stages (128 KiB of LDS).  A
-// 256-wide tile moves 2/3 of the L2->LDS bytes per flop of a 128 x 256 one.
+// MFMAs) fed by a 2-deep ring of 128-byte K stages (128 KiB of LDS), the
+// copies of each stage spread between the MFMAs of the two sub-steps around
+// the stage barrier (a burst of all 64 of a CU's 1 KiB copies right after the
+// barrier kept waves from their MFMAs; spread: 3-4% faster).  A 256-wide tile
+// moves 2/3 of the L2->LDS bytes per flop of a 128 x 256 one.
 #ifndef GATE_BM
 #define GATE_BM 256
 #endif

@@ -259,19 +259,19 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define HB_PER_CU 2
 #endif
 #ifndef DN_PER_CU
-#define DN_PER_CU 3
+#define DN_PER_CU 2
 #endif
 #ifndef DU_STAGES
-#define DU_STAGES 3
+#define DU_STAGES 4
 #endif
 #ifndef DU_PER_CU
-#define DU_PER_CU 2
+#define DU_PER_CU 1
 #endif
 #ifndef DN_KB
 #define DN_KB 128
 #endif
 #ifndef DN_STAGES
-#define DN_STAGES 2
+#define DN_STAGES 3
 #endif
 #ifndef DN_WN
 #define DN_WN 64
@@ -292,7 +292,7 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define DN_PART_MB 256
 #endif
 #ifndef DU_BM
-#define DU_BM 64
+#define DU_BM 128
 #endif
 #ifndef DU_DB
 #define DU_DB 32
@@ -478,9 +478,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 // they stream whole weight matrices, so each workgroup keeps several K stages
 // of copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 3-deep
 // ring of 128-byte K stages (72 KiB), two workgroups per CU; down: 64 x 128,
-// 4 waves of 32 x 64, 2-deep ring of raw W_d stages (bf16: read with
-// transposing LDS reads, 48 KiB; fp32: transposed in LDS, 64 KiB), split
-// over K, three workgroups per CU where they fit.
+// 4 waves of 32 x 64, 3-deep ring of raw W_d stages (bf16: read with
+// transposing LDS reads, 72 KiB; fp32: transposed in LDS, 88 KiB), split
+// over K, two workgroups per CU where they fit.
 constexpr int HB_BM = 64, HB_WM = 32;
 #ifndef DN_BM
 #define DN_BM 64
@@ -488,12 +488,14 @@ constexpr int HB_BM = 64, HB_WM = 32;
 #ifndef DN_WM
 #define DN_WM 32
 #endif
-// Dual gate / up GEMM: 64 rows x 64 output columns per workgroup (a 128-row
-// B tile of 32-row W_g / W_u blocks), 4 waves of 32 x 64, 3-deep ring of
-// 24 KiB stages (72 KiB), two workgroups per CU (64-row blocks, 128 columns
-// and one 120 KiB workgroup per CU measured 2.5-12 us slower per call).
+// Dual gate / up GEMM: 128 rows x 64 output columns per workgroup (a
+// 128-row B tile of 32-row W_g / W_u blocks), 4 waves of 64 x 64, 4-deep
+// ring of 32 KiB stages (128 KiB), one workgroup per CU.  Against 64-row
+// tiles (two 72 KiB workgroups per CU) it moves a third fewer L2->LDS bytes
+// for a few hundred rows: measured 1-2 us faster per call at 211 and 328
+// overflow rows, no slower at 1.
 #ifndef DU_WM
-#define DU_WM 32
+#define DU_WM 64
 #endif
 
 // Workgroups for a tile loop: one per CU, at most `tiles`, rounded down to a

@@ -266,6 +266,39 @@ struct GemmCore {
         }
     }
 
+    // Copy c of stage kt's A_LD + B_LD copies (A first) into ring slot `buf`.
+    __device__ __forceinline__ void load_one(int kt, char *buf, int c)
+    {
+        const int koff = kt * KB;
+        if (c < A_LD) {
+            dma16(ra, buf + (c * NW + wave) * 1024, a_voff[c], koff);
+        } else {
+            const int j = c - A_LD;
+            dma16(rb, buf + LDS_A + (j * NW + wave) * 1024, b_voff[j], koff);
+        }
+    }
+
+    // One MFMA sub-step with copies C0..C1-1 of stage kt spread evenly
+    // between its MFMAs (kept in that order), so the copy queue fills at the
+    // rate it drains instead of all at once.
+    // `on` (wave-uniform) only gates the copies: the MFMAs run on every path,
+    // so the accumulators never merge from two versions.
+    template <int C0, int C1>
+    __device__ __forceinline__ void mfma_sub_copies(const u32x4 (&af)[FM], const u32x4 (&bf)[FN],
+                                                    f32x16 (&acc)[FM][FN], int kt, char *buf, bool on)
+    {
+        constexpr int NM = FM * FN, NC = C1 - C0;
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+            mfma_chunk(TI{}, af[q / FN], bf[q % FN], acc[q / FN][q % FN]);
+#pragma unroll
+            for (int c = C0; c < C1; ++c)
+                if ((c - C0) * NM / NC == q && on)
+                    load_one(kt, buf, c);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
     // Queue stage kt's global->LDS copies into ring slot `buf`.
     __device__ __forceinline__ void load(int kt, char *buf)
     {
@@ -484,6 +517,9 @@ struct GemmCore {
                     const int cb = ss & 1, nb = cb ^ 1;
                     if (ss + 1 < SUB) {
                         read_frags(cur, cur + LDS_A, wm, wn, lane, ss + 1, af[nb], bf[nb]);
+                        // issued before this sub-step's MFMAs, not after them: left alone
+                        // the scheduler gives them the registers those MFMAs free
+                        __builtin_amdgcn_sched_barrier(0);
                     } else {
                         // earlier sub-steps' MFMAs stay above the waits
                         __builtin_amdgcn_sched_barrier(0);
@@ -508,14 +544,86 @@ struct GemmCore {
         __syncthreads();
     }
 
-    // Full K loop.  NK operands: run_nk.  KN B: an STAGES-deep ring of LDS
+    // K loop for NK operands, 2-slot ring, copies spread over the MFMAs: the
+    // copies of stage kt + 2 (into stage kt's slot, free once the barrier
+    // before stage kt's last sub-step has passed) are issued in two halves,
+    // between the MFMAs of that last sub-step and of stage kt + 1's first.
+    // The barrier before stage kt + 2 waits for all of them (vmcnt(0)).
+    __device__ __forceinline__ void run_nk_spread(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb,
+                                                  int klen, int tid, f32x16 (&acc)[FM][FN])
+    {
+        static_assert(STAGES == 2 && !B_KN && DUALB == 0 && SUB % 2 == 0, "spread copies: NK, 2 slots");
+        constexpr int NC = A_LD + B_LD, H = NC / 2;
+        const int lane = tid & 63;
+        const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wv / NWN, wn = wv % NWN;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[fm][fn][i] = 0.f;
+        setup(p, m0, n0, m_used, kb, tid);
+        const int nk = klen / KT;
+        if (nk > 0) {
+            load(0, smem);
+            wait_n<0>();
+            wg_barrier();
+            u32x4 af[2][FM], bf[2][FN];
+            read_frags(smem, smem + LDS_A, wm, wn, lane, 0, af[0], bf[0]);
+            if (nk > 1)
+                load(1, smem + BUF);
+            int slot = 0;
+#pragma clang loop unroll(disable)
+            for (int kt = 0; kt < nk; ++kt) {
+                char *cur = smem + slot * BUF;
+                const int nslot = slot ^ 1;
+                // the second half of stage kt + 1's copies (first half queued during stage kt - 1)
+                const bool pend = kt >= 1 && kt + 1 < nk;
+#pragma unroll
+                for (int ss = 0; ss < SUB; ++ss) {
+                    const int cb = ss & 1, nb = cb ^ 1;
+                    if (ss + 1 < SUB) {
+                        read_frags(cur, cur + LDS_A, wm, wn, lane, ss + 1, af[nb], bf[nb]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    } else {
+                        __builtin_amdgcn_sched_barrier(0);
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    }
+                    if (ss + 1 == SUB) {
+                        if (kt + 1 < nk) {
+                            wait_n<0>();
+                            wg_barrier();
+                            const char *nxt = smem + nslot * BUF;
+                            read_frags(nxt, nxt + LDS_A, wm, wn, lane, 0, af[nb], bf[nb]);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        mfma_sub_copies<0, H>(af[cb], bf[cb], acc, kt + 2, cur, kt + 2 < nk);
+                    } else if (ss == 0) {
+                        mfma_sub_copies<H, NC>(af[cb], bf[cb], acc, kt + 1, smem + nslot * BUF, pend);
+                    } else {
+                        mfma_sub(af[cb], bf[cb], acc);
+                    }
+                }
+                slot = nslot;
+            }
+        }
+        __syncthreads();
+    }
+
+    // Full K loop.  NK operands, 2-slot ring (the gate): run_nk_spread; other
+    // NK rings and transposing-read KN (bf16): run_nk.  KN B: an STAGES-deep ring of LDS
     // slots fed by global->LDS copies issued STAGES-1 stages ahead, two
     // barriers per stage (the stage is transposed in LDS first).  Ends with a
     // barrier so the caller may reuse `smem`.
     __device__ __forceinline__ void run(const GemmArgs &p, char *smem, int m0, int n0, int m_used, int kb, int klen,
                                         int tid, f32x16 (&acc)[FM][FN])
     {
-        if constexpr (!B_KN || B_TR) {
+        if constexpr (STAGES == 2 && !B_KN && DUALB == 0 && SUB % 2 == 0) {
+            run_nk_spread(p, smem, m0, n0, m_used, kb, klen, tid, acc);
+            return;
+        } else if constexpr (!B_KN || B_TR) {
             run_nk(p, smem, m0, n0, m_used, kb, klen, tid, acc);
             return;
         }
