@@ -259,7 +259,7 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define HB_PER_CU 2
 #endif
 #ifndef DN_PER_CU
-#define DN_PER_CU 2
+#define DN_PER_CU 3
 #endif
 #ifndef DU_STAGES
 #define DU_STAGES 4
@@ -271,7 +271,7 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define DN_KB 128
 #endif
 #ifndef DN_STAGES
-#define DN_STAGES 3
+#define DN_STAGES 2
 #endif
 #ifndef DN_WN
 #define DN_WN 64
@@ -283,7 +283,7 @@ hipError_t launch_compact_rows(const int32_t *row_ovf, int T, int max_ovf, int32
 #define DN_MAX_SPLITS 16
 #endif
 #ifndef DN_TARGET_WGS
-#define DN_TARGET_WGS 256
+#define DN_TARGET_WGS 512
 #endif
 #ifndef DN_ROWS_HINT
 #define DN_ROWS_HINT 256
@@ -478,9 +478,10 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 // they stream whole weight matrices, so each workgroup keeps several K stages
 // of copies in flight): gate / up: 64 x 128 per workgroup, 4 waves, 3-deep
 // ring of 128-byte K stages (72 KiB), two workgroups per CU; down: 64 x 128,
-// 4 waves of 32 x 64, 3-deep ring of raw W_d stages (bf16: read with
-// transposing LDS reads, 72 KiB; fp32: transposed in LDS, 88 KiB), split
-// over K, two workgroups per CU where they fit.
+// 4 waves of 32 x 64, 2-deep ring of raw W_d stages (bf16: read with
+// transposing LDS reads, 48 KiB; fp32: transposed in LDS, 64 KiB), split
+// over K, three workgroups per CU where they fit (a 3-deep ring with two per
+// CU measured no faster).
 constexpr int HB_BM = 64, HB_WM = 32;
 #ifndef DN_BM
 #define DN_BM 64
@@ -597,9 +598,11 @@ int down_splits(int max_ovf, int F, int d)
 {
     // The rows in use (n_ovf) are known only on the device; size the split for
     // about DN_ROWS_HINT of them (a few hundred overflow rows is the usual
-    // case), enough (tile, split) pairs for every CU, K slices whole multiples
-    // of 64, and the partial slabs ([splits][max_ovf][d] fp32) at most
-    // DN_PART_MB of workspace.
+    // case): about two (tile, split) pairs per CU, K slices whole multiples of
+    // 64, and the partial slabs ([splits][max_ovf][d] fp32) at most DN_PART_MB
+    // of workspace.  At the 2B-like layer (211 rows) that is 8 splits of 1024
+    // K elements: 18 us for the down GEMM, against 26 us with 4 splits (K
+    // chains twice as long) and 25 us with 16 (twice the partial traffic).
     const long tiles = (long)((DN_ROWS_HINT + DN_BM - 1) / DN_BM) * ((d + DN_BN - 1) / DN_BN);
     const long slab = (long)max_ovf * d * 4;
     int s = 1;
