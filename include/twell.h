@@ -165,7 +165,11 @@ TWELL_API int twell_pack_gate_stats(const void *x, const void *wg_t, int32_t d, 
 TWELL_API int twell_partition_overflow(const void *x, const void *wg_t, int32_t d,
                              const twell_hybrid_t *hy, void *stream);
 
-/* twell_pack_gate on hy->ell followed by twell_partition_overflow. */
+/* The hybrid ELL + dense-backup activation in one call (sections 2.1 and
+ * 2.3 of the page: TwELL packed in the gate's epilogue, then the rows whose
+ * tiles overflow the capacity moved to a dense backup): twell_pack_gate on
+ * hy->ell followed by twell_partition_overflow, with their arguments, checks
+ * and outputs.  Needs no workspace: every output is one of hy's arrays. */
 TWELL_API int twell_pack_gate_hybrid(const void *x, const void *wg_t, int32_t d,
                            const twell_hybrid_t *hy, void *stream);
 
@@ -209,9 +213,13 @@ TWELL_API size_t twell_workspace_bytes(int32_t T, int32_t F, int32_t tile_w, int
 TWELL_API int twell_ffn_overflow(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
                        int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Hybrid FFN: twell_ffn_fused for all rows in hy->order (overflow rows get
- * 0), then twell_ffn_overflow for the overflow rows; every row of y is the
- * full FFN output when n_ovf <= max_ovf. */
+/* Hybrid FFN (sections 2.2 and 2.3 of the page: the fused up/down step over
+ * the sparse part, the dense FFN over the dense backup's rows):
+ * twell_ffn_fused for all rows in hy->order (overflow rows get 0), then
+ * twell_ffn_overflow for the overflow rows; every row of y is the full FFN
+ * output when n_ovf <= max_ovf.  Expects hy filled by twell_pack_gate_hybrid
+ * on the same stream.  workspace: as twell_ffn_overflow's (it serves both
+ * steps); y : device [T][d] float. */
 TWELL_API int twell_ffn_hybrid(const twell_hybrid_t *hy, const void *x, const void *wu_t, const void *wd,
                      int32_t d, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
