@@ -309,19 +309,23 @@ TWELL_API int twell_compact_hybrid(const twell_hybrid_t *hy, void *buf, size_t b
 TWELL_API int twell_compact_to_dense(const void *buf, int32_t T, int32_t F, int32_t vdtype, void *out, void *stream);
 
 /* Bytes of device workspace twell_ffn_decode needs for these sizes (0 when
- * the sizes are outside its range). */
+ * the sizes are outside its range).  For T <= 16 it holds a partial y row
+ * per (row, group of 32 neurons): T * (F / 32) * d floats, plus z. */
 TWELL_API size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t tile_w);
 
 /* The whole FFN for decode-shaped calls, T <= 64 rows, bf16 (sections
  * 2.1-2.3 of the page: the same gate, TwELL, overflow partition and fused
- * up/down, organised for a few tokens: the gate spread over F/32 workgroups,
- * and every row's entries cut into chunks shared out over the GPU so that a
- * heavy row does not run alone).  Writes everything twell_pack_gate_hybrid
- * writes (TwELL, row_ovf, ovf_rows, n_ovf, the dense backup of the first
- * min(n_ovf, max_ovf) overflow rows, order) and every row of y, overflow rows
- * included (whatever max_ovf is): y[t] = sum over t's active neurons j, in
- * ascending j, of (h * (x[t] . W_u^T[j])) * W_d[j], h the stored bf16 gate
- * value, in fp32.  Same bits for repeated calls.
+ * up/down, organised for a few tokens: the gate spread over F/32
+ * workgroups).  For T <= 16 each gate workgroup does the up/down work of its
+ * own 32 neurons as soon as their gate values are known, and a second kernel
+ * adds the partial rows while it packs TwELL; for larger T every row's
+ * entries are cut into chunks shared out over the GPU.  Writes everything
+ * twell_pack_gate_hybrid writes (TwELL, row_ovf, ovf_rows, n_ovf, the dense
+ * backup of the first min(n_ovf, max_ovf) overflow rows, order) and every row
+ * of y, overflow rows included (whatever max_ovf is): y[t] = sum over t's
+ * active neurons j of (h * (x[t] . W_u^T[j])) * W_d[j], h the stored bf16
+ * gate value, in fp32, summed in a fixed order (which depends on T).  Same
+ * bits for repeated calls.
  *   x : device [T][d] bf16; wg_t, wu_t, wd : device [F][d] bf16; y : [T][d] float.
  *   hy : T <= 64, vdtype TWELL_BF16, T * F <= 2^20, F / tile_w <= 512.
  *   workspace : device, >= twell_ffn_decode_workspace_bytes(T, F, d, tile_w),
@@ -334,8 +338,11 @@ TWELL_API int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t
 
 /* twell_ffn_decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid hipMalloc).  Same arguments (minus the workspace),
- * same checks, same kernels and the same output bits as twell_ffn_decode.
+ * harnesses that forbid hipMalloc).  Same arguments (minus the workspace) and
+ * checks as twell_ffn_decode; it always runs the chunked (T > 16) kernels,
+ * whose scratch stays small, so TwELL, the partition, the order and the dense
+ * backup are the same bits as twell_ffn_decode's and y the same sums in
+ * another order for T <= 16 (the same bits for T > 16).
  * Its scratch is a 16 MiB array in the library's device code: each GPU the
  * library runs on holds one copy from the first call on it until the process
  * ends.  The first call on a device looks up that copy's address
@@ -344,9 +351,10 @@ TWELL_API int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t
  * call left; what must start at zero is cleared by the call's own kernels.
  * Calls that overlap in time on one GPU (e.g. on two streams) race on the
  * scratch: serialise them.
- * Limit: twell_ffn_decode_workspace_bytes(T, F, d, tile_w) <= 16 MiB, which
- * holds every shape twell_ffn_decode accepts with d <= 2048; larger needs
- * return TWELL_E_SCRATCH before anything is queued. */
+ * Limit: its scratch need, T * F fp32 values of z plus (1024 + T) partial
+ * rows of d floats (and a few KiB of tables), must fit 16 MiB, which holds
+ * every shape twell_ffn_decode accepts with d <= 2048; larger needs return
+ * TWELL_E_SCRATCH before anything is queued. */
 TWELL_API int twell_ffn_decode_noalloc(const void *x, const void *wg_t, const void *wu_t, const void *wd,
                                        int32_t d, const twell_hybrid_t *hy, float *y, void *stream);
 

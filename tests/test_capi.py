@@ -195,12 +195,21 @@ def test_ffn_decode_noalloc_validation():
     assert f(GOOD, GOOD, GOOD, GOOD, 60, ctypes.byref(ok), GOOD, None) == -3                    # d % 64
     assert f(None, None, None, None, 64, ctypes.byref(hy(T=0)), None, None) == 0                # nothing to do
     # d = 4096: (1024 + T) partial rows of 16 KiB exceed the 16 MiB scratch
-    assert lib.twell_ffn_decode_workspace_bytes(1, 512, 4096, 128) > 16 << 20
+    assert noalloc_scratch_need(1, 512, 4096) > 16 << 20
     assert f(GOOD, GOOD, GOOD, GOOD, 4096, ctypes.byref(hy(T=1)), GOOD, None) == -7
     assert b"static" in lib.twell_status_str(-7)
     # every d <= 2048 shape the decode path accepts fits (largest: T * F = 2^20, d = 2048)
-    assert lib.twell_ffn_decode_workspace_bytes(64, 16384, 2048, 32) <= 16 << 20
-    assert lib.twell_ffn_decode_workspace_bytes(1, 1 << 20, 2048, 256) <= 16 << 20
+    assert noalloc_scratch_need(64, 16384, 2048) <= 16 << 20
+    assert noalloc_scratch_need(1, 1 << 20, 2048) <= 16 << 20
+
+
+def noalloc_scratch_need(T, F, d):
+    """Bytes the allocation-free decode path carves from its static scratch
+    (its four-kernel layout, 256-byte aligned sections): z [T][F] fp32, the
+    counter block, per-row sums [2T], the chunk table [T + 1], and
+    (1024 + T) partial rows of d floats."""
+    up = lambda b: (b + 255) & ~255  # noqa: E731
+    return up(T * F * 4) + 256 + up(T * 8) + up((T + 1) * 4) + up((1024 + T) * d * 4)
 
 
 def test_conversion_validation():

@@ -13,6 +13,7 @@ from hypothesis import strategies as st
 
 import oracle
 import unstructured_sparse_transformer_amd as tw
+from test_capi import noalloc_scratch_need
 from workloads import make_random_small
 
 SETTINGS = settings(max_examples=60, deadline=None, derandomize=True,
@@ -125,7 +126,7 @@ def test_decode_noalloc_scratch_rule(T, F, w, d):
         want = -4
     elif T == 0:
         want = 0
-    elif lib.twell_ffn_decode_workspace_bytes(T, F, d, w) > 16 << 20:
+    elif noalloc_scratch_need(T, F, d) > 16 << 20:
         want = -7
     else:
         return  # accepted: would launch

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "decode2.h"
 #include "launch.h"
 
 namespace {
@@ -478,7 +479,8 @@ size_t twell_ffn_decode_workspace_bytes(int32_t T, int32_t F, int32_t d, int32_t
     if (T < 0 || T > twell::DEC_MAX_T || F <= 0 || d <= 0 || (tile_w != 32 && tile_w != 64 && tile_w != 128 &&
                                                              tile_w != 256) || F % tile_w != 0)
         return 0;
-    return twell::decode_ws_layout(nullptr, T, F, tile_w, d).bytes;
+    return T <= twell::DEC2_MAX_T ? twell::decode_ws2_layout(nullptr, T, F, d).bytes
+                                  : twell::decode_ws_layout(nullptr, T, F, tile_w, d).bytes;
 }
 
 int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
@@ -492,10 +494,18 @@ int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t, const vo
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return TWELL_E_ALIGN;
     const twell_t *h = &hy->ell;
-    const twell::DecodeWs w = twell::decode_ws_layout(workspace, h->T, h->F, h->tile_w, d);
+    if (h->T > twell::DEC2_MAX_T) {
+        const twell::DecodeWs w = twell::decode_ws_layout(workspace, h->T, h->F, h->tile_w, d);
+        if (workspace_bytes < w.bytes)
+            return TWELL_E_WORKSPACE;
+        return launch_decode(x, wg_t, wu_t, wd, d, hy, y, w, static_cast<hipStream_t>(stream));
+    }
+    const twell::DecodeWs2 w = twell::decode_ws2_layout(workspace, h->T, h->F, d);
     if (workspace_bytes < w.bytes)
         return TWELL_E_WORKSPACE;
-    return launch_decode(x, wg_t, wu_t, wd, d, hy, y, w, static_cast<hipStream_t>(stream));
+    return hip_status(twell::launch_decode2(x, wg_t, wu_t, wd, h->T, d, h->F, h->tile_w, h->cap, h->val, h->idx,
+                                            h->cnt, hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->order, hy->max_ovf,
+                                            hy->dense, y, w, static_cast<hipStream_t>(stream)));
 }
 
 int twell_ffn_decode_noalloc(const void *x, const void *wg_t, const void *wu_t, const void *wd, int32_t d,
