@@ -43,6 +43,13 @@ DEC_EDGE = [
     (17, 192, 768, 256, 1, 0.2, 0.5, 0),      # cap = 1: nearly every row overflows
     (64, 128, 16384, 256, 16, 0.5, 0.2, 0),   # T * F = 2^20, half active: large gather chunks
     (40, 64, 320, 64, 64, 0.3, 0.5, 0),       # cap = w: no overflow possible
+    # Windows of at most 16 rows take the two-kernel organisation (rows split
+    # over 8, 4, 2 or 1 waves by T; 1, 2, 4 or 8 16-byte chunks per lane by d).
+    (2, 1024, 2048, 256, 8, 0.1, 0.5, 0),     # T = 2: four waves per row, two chunks per lane
+    (3, 4096, 1024, 128, 4, 0.1, 0.5, 0),     # T = 3: two waves per row, d = 4096 (no prefetch)
+    (4, 1536, 1024, 64, 2, 0.1, 0.5, 5),      # T = 4: ragged last reduce block, dead neurons
+    (16, 4096, 2048, 256, 4, 0.1, 0.5, 0),    # T = 16 at d = 4096: largest two-kernel window
+    (16, 192, 768, 256, 1, 0.2, 0.5, 0),      # T = 16, cap = 1: the T = 17 case's twin below the switch
 ]
 
 
