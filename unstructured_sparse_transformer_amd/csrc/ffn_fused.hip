@@ -154,8 +154,9 @@ __device__ __forceinline__ void group_stream(const FusedArgs<TI> &a, const int2 
 // current row's weight stream.  A row slice is LPE 16-byte pieces: the lanes
 // take 64 / LPE entries per step, LPE lanes per entry and one piece per lane.
 // The up pass keeps the lane's piece of x[t] in registers and writes, per
-// entry, the partial dot product of x[t] and W_u^T[j] over the slice (DPP
-// reduction over the entry's lanes) to p[c][slot] (fp32; slice-major, so one
+// entry, the partial dot product of x[t] and W_u^T[j] over the slice (bf16:
+// v_dot2_f32_bf16, two products per instruction; DPP reduction over the
+// entry's lanes) to p[c][slot] (fp32; slice-major, so one
 // XCD's writes for consecutive entries share cache lines).  The down pass
 // forms s = h * (p[0][slot] + ... + p[nch - 1][slot]) (fixed order) and
 // accumulates y[t][slice] += s * W_d[j] in the lanes' registers, each lane its
@@ -249,6 +250,23 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_entries_kernel(PassArgs<T
     }
 }
 
+// x . w over the 8 bf16 elements of two 16-byte pieces, two products and the
+// running sum per v_dot2_f32_bf16, pairs in ascending element order.  (The
+// pairs are taken by shuffles of the whole piece: bit-casting a subscripted
+// element of the 4 x u32 vector made the compiler read element 0 for all four.)
+__device__ __forceinline__ float dot8_bf16(const u32x4 &x, const u32x4 &w)
+{
+    const bf16x8 xb = __builtin_bit_cast(bf16x8, x), wb = __builtin_bit_cast(bf16x8, w);
+    float p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(xb, xb, 0, 1),
+                                              __builtin_shufflevector(wb, wb, 0, 1), 0.f, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(xb, xb, 2, 3), __builtin_shufflevector(wb, wb, 2, 3), p,
+                                        false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(xb, xb, 4, 5), __builtin_shufflevector(wb, wb, 4, 5), p,
+                                        false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(xb, xb, 6, 7),
+                                           __builtin_shufflevector(wb, wb, 6, 7), p, false);
+}
+
 // Sum of v over each aligned group of L lanes (L = 8, 16, 32, 64), left in
 // the group's last lane (DPP row shifts, then row broadcasts).
 template <int L> __device__ __forceinline__ float group_sum_last(float v)
@@ -270,6 +288,7 @@ template <int L> __device__ __forceinline__ float group_sum_last(float v)
 // partial dot products).  x piece: the up pass's lane piece of x[t].
 template <typename TI, bool DOWN> struct RowWin {
     int2 en;
+    uint32_t off;  // byte offset of entry k's weight row, j * d * sizeof(TI) (< 2^32 by the host checks)
     float pv[DOWN ? 8 : 1];
     u32x4 xv;
 };
@@ -283,6 +302,7 @@ __device__ __forceinline__ void row_win_load(const PassArgs<TI> &a, int t, int e
     const int k = w0 + lane;
     const bool ok = k < e;
     r.en = ok ? a.w.ent[rbase + k] : make_int2(0, 0);
+    r.off = (uint32_t)r.en.x * (uint32_t)(a.d * Elt<TI>::SIZE);
     if (DOWN) {
         if (a.w.nch == 8) {
 #pragma unroll
@@ -304,6 +324,7 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
 {
     constexpr int E = Elt<TI>::PER_CHUNK;  // elements per 16-byte piece
     constexpr int EPI = 64 / LPE;          // entries per step
+    constexpr bool BF16 = sizeof(TI) == 2;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nch = a.w.nch;
@@ -329,9 +350,11 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
 #define tr(r) __builtin_amdgcn_readlane(tv, (r))
 #define er(r) __builtin_amdgcn_readlane(ev, (r))
     const int q = lane / LPE, pc = lane % LPE;  // entry of the step, 16-byte piece of the row slice
-    const int64_t row_bytes = (int64_t)a.d * Elt<TI>::SIZE;
     const int64_t col_off = (int64_t)(csl * a.cw + pc * E) * Elt<TI>::SIZE;
-    const char *wbase = (const char *)(DOWN ? a.wd : a.wu_t) + col_off;
+    // weight rows: a base uniform over the workgroup (its slice) plus a 32-bit
+    // per-lane offset (entry row + the lane's piece), one VGPR add per load
+    const char *wbase = (const char *)(DOWN ? a.wd : a.wu_t) + (int64_t)csl * a.cw * Elt<TI>::SIZE;
+    const uint32_t piece_off = (uint32_t)(pc * 16);
     const int slots = a.n_b * a.cap;
     // first row with entries, its first window requested at once
     int r = 0;
@@ -351,7 +374,8 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
         const int t = tr(r), e = er(r);
         const int64_t rbase = (int64_t)t * slots;
         float xf[E], acc[E];
-        if (!DOWN) {
+        const u32x4 xr = cur.xv;  // bf16: x pairs for the packed dot products
+        if (!DOWN && !BF16) {
 #pragma unroll
             for (int e2 = 0; e2 < E; ++e2)
                 xf[e2] = chunk_elem<TI>(cur.xv, e2);
@@ -372,7 +396,6 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
         for (int w0 = 0; w0 < e; w0 += 64) {
             if (w0 > 0)
                 row_win_load<TI, DOWN>(a, t, e, w0, lane, col_off, cur);
-            int j = cur.en.x;
             float sv = 0.f;
             if (DOWN) {
                 float u = 0.f;
@@ -392,14 +415,17 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
             if (PASS_PREFETCH && w0 + 64 >= e && rn < PASS_ROWS)
                 row_win_load<TI, DOWN>(a, tr(rn), er(rn), 0, lane, col_off, nxt);
             for (int k0 = 0; k0 < n; k0 += EPI * PASS_U) {
+                // (a fresh zero for lanes past the window's end: keeping the
+                // registers across steps and skipping those loads instead was
+                // 25% slower, the steps' loads then waiting on each other)
                 u32x4 wv[PASS_U];
                 float sc[PASS_U];
 #pragma unroll
                 for (int u = 0; u < PASS_U; ++u) {
                     const int kk = k0 + u * EPI + q;
-                    const int jj = __shfl(j, kk, 64);
+                    const uint32_t oj = (uint32_t)__shfl((int)cur.off, kk, 64);
                     sc[u] = DOWN ? __shfl(sv, kk, 64) : 0.f;
-                    wv[u] = kk < n ? ldg16(wbase + (int64_t)jj * row_bytes) : u32x4{0, 0, 0, 0};
+                    wv[u] = kk < n ? ldg16(wbase + (oj + piece_off)) : u32x4{0, 0, 0, 0};
                 }
                 if (DOWN) {
 #pragma unroll
@@ -415,9 +441,13 @@ __global__ __launch_bounds__(64 * PASS_WAVES) void ffn_pass_kernel(PassArgs<TI> 
 #pragma unroll
                     for (int u = 0; u < PASS_U; ++u) {
                         part[u] = 0.f;
+                        if constexpr (BF16) {
+                            part[u] = dot8_bf16(xr, wv[u]);
+                        } else {
 #pragma unroll
-                        for (int e2 = 0; e2 < E; ++e2)
-                            part[u] = fmaf(xf[e2], chunk_elem<TI>(wv[u], e2), part[u]);
+                            for (int e2 = 0; e2 < E; ++e2)
+                                part[u] = fmaf(xf[e2], chunk_elem<TI>(wv[u], e2), part[u]);
+                        }
                     }
 #pragma unroll
                     for (int u = 0; u < PASS_U; ++u)
