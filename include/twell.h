@@ -339,10 +339,12 @@ TWELL_API int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t
 /* twell_ffn_decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments (minus the workspace) and
- * checks as twell_ffn_decode; it always runs the chunked (T > 16) kernels,
- * whose scratch stays small, so TwELL, the partition, the order and the dense
- * backup are the same bits as twell_ffn_decode's and y the same sums in
- * another order for T <= 16 (the same bits for T > 16).
+ * checks as twell_ffn_decode, and the same kernels when their scratch fits:
+ * for T <= 16 the two-kernel organisation if its T * F / 32 partial rows of
+ * d floats fit, else (and for T > 16) the chunked kernels.  TwELL, the
+ * partition, the order and the dense backup are always the same bits as
+ * twell_ffn_decode's; y too when both take the same kernels, else the same
+ * sums in another order.
  * Its scratch is a 16 MiB array in the library's device code: each GPU the
  * library runs on holds one copy from the first call on it until the process
  * ends.  The first call on a device looks up that copy's address
@@ -351,9 +353,11 @@ TWELL_API int twell_ffn_decode(const void *x, const void *wg_t, const void *wu_t
  * call left; what must start at zero is cleared by the call's own kernels.
  * Calls that overlap in time on one GPU (e.g. on two streams) race on the
  * scratch: serialise them.
- * Limit: its scratch need, T * F fp32 values of z plus (1024 + T) partial
- * rows of d floats (and a few KiB of tables), must fit 16 MiB, which holds
- * every shape twell_ffn_decode accepts with d <= 2048; larger needs return
+ * Limit: one of the two scratch layouts must fit 16 MiB: for T <= 16,
+ * T * F fp32 values of z plus T * F / 32 partial rows of d floats (and
+ * T * F / 32 flags), or for any T, T * F values of z plus (1024 + T) partial
+ * rows of d floats (and a few KiB of tables).  The second holds every shape
+ * twell_ffn_decode accepts with d <= 2048; when neither fits the call returns
  * TWELL_E_SCRATCH before anything is queued. */
 TWELL_API int twell_ffn_decode_noalloc(const void *x, const void *wg_t, const void *wu_t, const void *wd,
                                        int32_t d, const twell_hybrid_t *hy, float *y, void *stream);

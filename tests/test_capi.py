@@ -194,10 +194,13 @@ def test_ffn_decode_noalloc_validation():
     assert f(GOOD, GOOD, GOOD, GOOD, 64, ctypes.byref(hy(T=64, F=32768, w=256)), GOOD, None) == -4
     assert f(GOOD, GOOD, GOOD, GOOD, 60, ctypes.byref(ok), GOOD, None) == -3                    # d % 64
     assert f(None, None, None, None, 64, ctypes.byref(hy(T=0)), None, None) == 0                # nothing to do
-    # d = 4096: (1024 + T) partial rows of 16 KiB exceed the 16 MiB scratch
-    assert noalloc_scratch_need(1, 512, 4096) > 16 << 20
-    assert f(GOOD, GOOD, GOOD, GOOD, 4096, ctypes.byref(hy(T=1)), GOOD, None) == -7
+    # d = 4096, T = 17: the chunked layout's (1024 + T) partial rows of 16 KiB
+    # exceed the 16 MiB scratch, and the two-kernel layout serves T <= 16 only
+    assert noalloc_scratch_need(17, 512, 4096) > 16 << 20
+    assert f(GOOD, GOOD, GOOD, GOOD, 4096, ctypes.byref(hy(T=17)), GOOD, None) == -7
     assert b"static" in lib.twell_status_str(-7)
+    # d = 4096, T = 1: the two-kernel layout fits
+    assert noalloc_scratch_need(1, 512, 4096) <= 16 << 20
     # every d <= 2048 shape the decode path accepts fits (largest: T * F = 2^20, d = 2048)
     assert noalloc_scratch_need(64, 16384, 2048) <= 16 << 20
     assert noalloc_scratch_need(1, 1 << 20, 2048) <= 16 << 20
@@ -205,11 +208,17 @@ def test_ffn_decode_noalloc_validation():
 
 def noalloc_scratch_need(T, F, d):
     """Bytes the allocation-free decode path carves from its static scratch
-    (its four-kernel layout, 256-byte aligned sections): z [T][F] fp32, the
-    counter block, per-row sums [2T], the chunk table [T + 1], and
-    (1024 + T) partial rows of d floats."""
+    (256-byte aligned sections): for T <= 16 the smaller of its two layouts.
+    Two-kernel layout: z [T][F] fp32, the counter block, flags [T][F / 32] and
+    T * F / 32 partial rows of d floats.  Chunked layout: z, the counter
+    block, per-row sums [2T], the chunk table [T + 1] and (1024 + T) partial
+    rows of d floats."""
     up = lambda b: (b + 255) & ~255  # noqa: E731
-    return up(T * F * 4) + 256 + up(T * 8) + up((T + 1) * 4) + up((1024 + T) * d * 4)
+    chunked = up(T * F * 4) + 256 + up(T * 8) + up((T + 1) * 4) + up((1024 + T) * d * 4)
+    if T > 16:
+        return chunked
+    two = up(T * F * 4) + 256 + up(T * (F // 32) * 4) + up(T * (F // 32) * d * 4)
+    return two if two <= 16 << 20 else chunked
 
 
 def test_conversion_validation():

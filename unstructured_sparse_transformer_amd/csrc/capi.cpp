@@ -515,10 +515,21 @@ int twell_ffn_decode_noalloc(const void *x, const void *wg_t, const void *wu_t, 
     if (hy->ell.T == 0)
         return TWELL_OK;
     const twell_t *h = &hy->ell;
-    if (twell::decode_ws_layout(nullptr, h->T, h->F, h->tile_w, d).bytes > twell::DEC_STATIC_BYTES)
+    // the two-kernel organisation when its layout fits the scratch (its first
+    // kernel clears the completion counter: nothing to clear here), else the
+    // chunked kernels when theirs does
+    const bool two = h->T <= twell::DEC2_MAX_T &&
+                     twell::decode_ws2_layout(nullptr, h->T, h->F, d).bytes <= twell::DEC_STATIC_BYTES;
+    if (!two && twell::decode_ws_layout(nullptr, h->T, h->F, h->tile_w, d).bytes > twell::DEC_STATIC_BYTES)
         return TWELL_E_SCRATCH;
     void *scratch = nullptr;
     TWELL_TRY(hip_status(twell::decode_static_workspace(&scratch)));
+    if (two) {
+        const twell::DecodeWs2 w = twell::decode_ws2_layout(scratch, h->T, h->F, d);
+        return hip_status(twell::launch_decode2(x, wg_t, wu_t, wd, h->T, d, h->F, h->tile_w, h->cap, h->val, h->idx,
+                                                h->cnt, hy->row_ovf, hy->ovf_rows, hy->n_ovf, hy->order, hy->max_ovf,
+                                                hy->dense, y, w, static_cast<hipStream_t>(stream)));
+    }
     const twell::DecodeWs w = twell::decode_ws_layout(scratch, h->T, h->F, h->tile_w, d);
     return launch_decode(x, wg_t, wu_t, wd, d, hy, y, w, static_cast<hipStream_t>(stream));
 }
